@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for the sparse-delta-memory decode step and token gather.
+
+This package draws inputs only: banks, slot lists, weights, values, gates and
+chunk lengths. It holds none of the method's arithmetic, and both the oracle
+side and the HIP side of every test and benchmark take their inputs from it.
+"""
+
+from .workloads import (  # noqa: F401
+    DecodeWorkload,
+    GatherWorkload,
+    WORKLOADS,
+    decode_bank,
+    decode_step_inputs,
+    decode_sequence,
+    gather_bank,
+    gather_inputs,
+    sub_seed,
+)

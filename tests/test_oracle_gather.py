@@ -1,0 +1,159 @@
+"""Pins of the token-gather oracle.
+
+Definition: page "sparse_delta_memory/cuda/gather_cuda.py", module docstring:
+per token and operand a float32-accumulated weighted sum of bank rows, a raw
+copy of operand 0's rows (the stash), and padding positions (t mod chunk >=
+valid) that read nothing and produce zeros; group g sums entries g, g+groups,
+... in order and the group partials are summed in order.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import bits_equal, f32_to_bf16_bits_torch, gamma, widen
+
+
+def _bank(values, bf16):
+    a = np.asarray(values, dtype=np.float32)
+    return f32_to_bf16_bits_torch(a) if bf16 else a.copy()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("groups", [1, 2, 3])
+def test_handworked_gather(golden_dir, bf16, groups):
+    c = json.load(open(os.path.join(golden_dir, "gather_handworked.json")))
+    bank = _bank(c["bank"], bf16)
+    out0, stash, out1 = oracle.gather(bank, c["idx0"], c["w0"], chunk=c["chunk"], valid=c["valid"],
+                                      idx1=c["idx1"], w1=c["w1"], groups=groups)
+    assert np.array_equal(out0, np.asarray(c["out0"], np.float32))
+    assert np.array_equal(out1, np.asarray(c["out1"], np.float32))
+    assert np.array_equal(widen(stash), np.asarray(c["stash"], np.float32))
+    # padding rows are +0.0 exactly (bit pattern zero), stash rows all-zero bits
+    assert not np.signbit(out0[1]).any() and not np.signbit(out1[3]).any()
+    assert not stash[1].any() and not stash[3].any()
+
+
+def _rand(rng, T, W, hd, slots, bf16):
+    bank = (rng.standard_normal((slots, hd)) * 0.3).astype(np.float32)
+    if bf16:
+        bank = f32_to_bf16_bits_torch(bank)
+    idx = rng.integers(0, slots, (T, W))
+    w = rng.standard_normal((T, W)).astype(np.float32)
+    return bank, idx, w
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_one_hot_weights_return_the_row(bf16):
+    rng = np.random.default_rng(20)
+    bank, idx, w = _rand(rng, 12, 9, 7, 50, bf16)
+    w[:] = 0.0
+    hot = rng.integers(0, 9, 12)
+    w[np.arange(12), hot] = 1.0
+    out, _, _ = oracle.gather(bank, idx, w, chunk=4)
+    assert np.array_equal(out, widen(bank[idx[np.arange(12), hot]]))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_width_one_is_one_product(bf16):
+    rng = np.random.default_rng(21)
+    bank, idx, w = _rand(rng, 16, 1, 5, 30, bf16)
+    out, _, _ = oracle.gather(bank, idx, w, chunk=16)
+    assert np.array_equal(out, widen(bank[idx[:, 0]]) * w[:, :1])
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_padding_and_stash(bf16):
+    rng = np.random.default_rng(22)
+    T, chunk = 24, 8
+    bank, idx, w = _rand(rng, T, 5, 6, 40, bf16)
+    cv = np.array([3, 0, 8], np.int32)
+    out, stash, _ = oracle.gather(bank, idx, w, chunk=chunk, chunk_valid=cv)
+    for t in range(T):
+        live = (t % chunk) < cv[t // chunk]
+        if live:
+            assert bits_equal(stash[t], bank[idx[t]])
+            assert np.any(out[t] != 0)
+        else:
+            assert not stash[t].any() and not out[t].any() and not np.signbit(out[t]).any()
+    # a scalar valid equals the same count repeated per chunk
+    o1, s1, _ = oracle.gather(bank, idx, w, chunk=chunk, valid=5)
+    o2, s2, _ = oracle.gather(bank, idx, w, chunk=chunk, chunk_valid=np.full(3, 5, np.int32))
+    assert bits_equal(o1, o2) and bits_equal(s1, s2)
+    # valid = 0: everything is padding; valid = chunk: nothing is
+    o0, st0, _ = oracle.gather(bank, idx, w, chunk=chunk, valid=0)
+    assert not o0.any() and not st0.any()
+    oc, stc, _ = oracle.gather(bank, idx, w, chunk=chunk, valid=chunk)
+    assert bits_equal(stc, bank[idx])
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("groups", [1, 2, 4, 7])
+def test_float32_within_bound_of_exact(bf16, groups):
+    rng = np.random.default_rng(23 + groups)
+    for W in (1, 4, 17, 64, 256):
+        bank, idx, w = _rand(rng, 6, W, 9, 400, bf16)
+        out, _, _ = oracle.gather(bank, idx, w, chunk=3, valid=2, groups=groups)
+        exact, mag = oracle.gather_f64(bank, idx, w, chunk=3, valid=2)
+        assert np.all(np.abs(out - exact) <= gamma(W + 1) * mag), (W, groups)
+
+
+def test_groups_agree_on_exact_integers():
+    rng = np.random.default_rng(24)
+    for W in (1, 3, 16, 65, 256):
+        bank = rng.integers(-8, 9, (300, 4)).astype(np.float32)
+        idx = rng.integers(0, 300, (5, W))
+        w = rng.integers(-4, 5, (5, W)).astype(np.float32)
+        ref, _, _ = oracle.gather(bank, idx, w, chunk=5)
+        exact, _ = oracle.gather_f64(bank, idx, w, chunk=5)
+        assert np.array_equal(ref, exact)
+        for groups in (2, 3, 8, 64):
+            out, _, _ = oracle.gather(bank, idx, w, chunk=5, groups=groups)
+            assert bits_equal(out, ref)
+
+
+def test_grouped_order_is_the_stated_one():
+    """Values chosen so that the float32 result depends on the order: group
+    partials over n = g, g+groups, ... then summed in group order."""
+    bank = np.array([[1.0], [2.0 ** 24], [-(2.0 ** 24)], [1.0]], np.float32)
+    idx = np.array([[1, 0, 2, 3]])
+    w = np.ones((1, 4), np.float32)
+    # groups = 1: ((2^24 + 1) + -2^24) + 1 -> 2^24 (tie to even) - 2^24 + 1 = 1
+    out1, _, _ = oracle.gather(bank, idx, w, chunk=1)
+    assert out1[0, 0] == 1.0
+    # groups = 2: p0 = 2^24 + -2^24 = 0, p1 = 1 + 1 = 2 -> 0 + 2 = 2
+    out2, _, _ = oracle.gather(bank, idx, w, chunk=1, groups=2)
+    assert out2[0, 0] == 2.0
+    # groups = 3 on rows [2^24, 1, 1]: ((0 + 2^24) + 1) + 1 = 2^24 in group order,
+    # while the reverse group order would give 2^24 + 2
+    bank3 = np.array([[2.0 ** 24], [1.0], [1.0]], np.float32)
+    out3, _, _ = oracle.gather(bank3, np.array([[0, 1, 2]]), np.ones((1, 3), np.float32), chunk=1,
+                               groups=3)
+    assert out3[0, 0] == 2.0 ** 24
+
+
+def test_second_operand_matches_a_one_operand_gather():
+    rng = np.random.default_rng(25)
+    bank, idx0, w0 = _rand(rng, 10, 6, 5, 60, True)
+    _, idx1, w1 = _rand(rng, 10, 11, 5, 60, True)
+    cv = np.array([2, 5], np.int32)
+    out0, stash, out1 = oracle.gather(bank, idx0, w0, chunk=5, chunk_valid=cv, idx1=idx1, w1=w1)
+    solo, _, _ = oracle.gather(bank, idx1, w1, chunk=5, chunk_valid=cv)
+    first, st, _ = oracle.gather(bank, idx0, w0, chunk=5, chunk_valid=cv)
+    assert bits_equal(out1, solo) and bits_equal(out0, first) and bits_equal(stash, st)
+
+
+def test_bad_arguments_are_reported():
+    bank = np.zeros((4, 2), np.float32)
+    idx = np.zeros((6, 2), np.int64)
+    w = np.zeros((6, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.gather(bank, idx, w, chunk=4)  # tokens not a multiple of chunk
+    with pytest.raises(ValueError):
+        oracle.gather(bank, idx, w, chunk=3, valid=4)
+    idx[0, 0] = 4
+    with pytest.raises(ValueError, match="out of range"):
+        oracle.gather(bank, idx, w, chunk=3)
