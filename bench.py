@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse-delta-memory hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--seed S]
+
+A step is one sdm_decode_step over every stream of the workload (one token
+per stream), or one sdm_gather launch over every token (--config c3). Inputs
+are seeded and synthetic (gen/), generated on the GPU and resident in HBM
+before the timed region; the decode cycles through the workload's token
+sequence, the bank changing from step to step as the method intends. The
+timed steps run as one HIP-graph replay (``--launch eager`` launches from
+Python instead) bracketed by HIP events on the stream the kernels run on.
+
+Prints one JSON line: stream-steps/s (tokens/s for the gather), the achieved
+bank-row bandwidth against the MI355X's 8 TB/s HBM peak, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "stream-steps/sec + achieved HBM GB/s (bank row bytes) on one MI355X"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP kernel sources; stored HBM-traffic figures are valid only for it."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "sparse_delta_rule_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this config, if they were
+    taken on the current kernel sources (profiles/traffic.json), else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(config)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's sequence)")
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    return p.parse_args(argv)
+
+
+def _timed(torch, stream, fn):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)  # ms
+
+
+def _run_steps(torch, args, launch_one, K):
+    """Warm up, then time K launches (as one graph replay, or eagerly). Returns ms."""
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        launch_one(i)
+    torch.cuda.synchronize()
+    if args.launch == "eager":
+        return _timed(torch, stream, lambda: [launch_one(i) for i in range(K)])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(K):
+            launch_one(i)
+    graph.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    return _timed(torch, torch.cuda.current_stream(), graph.replay)
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline_decode(torch, wl, bank, seq, target_s, cfg_name):
+    """Time the oracle (single thread) on a subset of streams over the whole sequence."""
+    import numpy as np
+    import oracle
+    P = wl.slots_per_stream
+
+    def to_np(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    def subset(n):
+        streams = torch.arange(n, device=bank.device)
+        rows = (streams[:, None] * P + torch.arange(P, device=bank.device)[None, :]).ravel()
+        b = to_np(bank[rows]).copy()
+        steps = []
+        for inp in seq:
+            d = {}
+            for k, v in inp.items():
+                v = v[:n].detach().cpu()
+                d[k] = v.to(torch.int64).numpy() if k in ("k_idx", "q_idx") else v.float().numpy()
+            steps.append(d)
+        return b, steps
+
+    # calibrate on 4 streams x 2 steps, then size the sample for ~target_s of work
+    b, steps = subset(min(4, wl.streams))
+    t0 = time.perf_counter()
+    for inp in steps[:2]:
+        oracle.decode_step(b, **inp)
+    per = (time.perf_counter() - t0) / (2 * min(4, wl.streams))
+    n = int(max(1, min(wl.streams, target_s / max(per * len(seq), 1e-9))))
+    b, steps = subset(n)
+    t0 = time.perf_counter()
+    for inp in steps:
+        oracle.decode_step(b, **inp)
+    dt = time.perf_counter() - t0
+    return {"value": n * len(steps) / dt, "unit": "stream-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.streams} streams x all {len(steps)} steps of {cfg_name} "
+                      f"(single-threaded C oracle, {dt:.1f} s)"}
+
+
+def cpu_baseline_gather(torch, wl, bank, inp, live, target_s, cfg_name):
+    import numpy as np
+    import oracle
+
+    def to_np(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.float().numpy()
+
+    def run(n):
+        sel = torch.arange(n, device=bank.device)
+        i0, i1 = inp["idx0"][sel].long(), inp["idx1"][sel].long()
+        uniq, inv = torch.unique(torch.cat([i0.ravel(), i1.ravel()]), return_inverse=True)
+        sub = to_np(bank[uniq])
+        a0 = inv[:i0.numel()].view_as(i0).cpu().numpy()
+        a1 = inv[i0.numel():].view_as(i1).cpu().numpy()
+        w0 = inp["w0"][sel].float().cpu().numpy()
+        w1 = inp["w1"][sel].float().cpu().numpy()
+        cv = inp["chunk_valid"][: n // wl.chunk].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.gather(sub, a0, w0, chunk=wl.chunk, chunk_valid=cv, idx1=a1, w1=w1)
+        return time.perf_counter() - t0
+
+    per = run(wl.chunk * 4) / (wl.chunk * 4)
+    n = int(max(wl.chunk, min(wl.tokens, target_s / max(per, 1e-9))) // wl.chunk * wl.chunk)
+    dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {wl.tokens} tokens of {cfg_name} (single-threaded C oracle, {dt:.1f} s)"}
+
+
+# ------------------------------------------------------------------ workloads
+def bench_decode(torch, args, cfg_name, wl):
+    import gen
+    from sparse_delta_rule_amd import sdm_decode_step
+    dev = torch.device("cuda", 0)
+    es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    bank = gen.decode_bank(wl, args.seed, dev)
+    seq = [gen.decode_step_inputs(wl, args.seed, t, dev) for t in range(wl.steps)]
+    readings = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_decode(torch, wl, bank, seq, args.cpu_seconds, cfg_name)
+    K = args.steps if args.steps is not None else wl.steps
+
+    def launch_one(i):
+        j = i % len(seq)
+        sdm_decode_step(bank, **seq[j], readings=readings[j])
+
+    ms = _run_steps(torch, args, launch_one, K)
+    ms_step = ms / K
+    row_bytes = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
+    gbps = row_bytes / (ms_step * 1e-3) / 1e9
+    config = {"workload": f"{cfg_name}: {wl.name}", "streams": wl.streams, "slots": wl.num_slots,
+              "head_dim": wl.head_dim, "W": wl.W, "R": wl.R, "G": wl.G,
+              "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "index_dtype":
+              str(wl.idx_dtype).replace("torch.", ""), "sequence_steps": wl.steps, "launch": args.launch,
+              "seed": args.seed}
+    value = wl.streams * K / (ms * 1e-3)
+    return dict(value=value, unit="stream-steps/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
+                row_bytes=row_bytes, kernel="sdm_decode_kernel", cpu=cpu, tokens_per_s=value)
+
+
+def bench_gather(torch, args, cfg_name, wl):
+    import gen
+    from sparse_delta_rule_amd import sdm_gather
+    dev = torch.device("cuda", 0)
+    es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    bank = gen.gather_bank(wl, args.seed, dev)
+    inp = gen.gather_inputs(wl, args.seed, dev)
+    T = wl.tokens
+    t = torch.arange(T, device=dev)
+    live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
+    out0 = torch.empty((T, wl.head_dim), device=dev)
+    out1 = torch.empty((T, wl.head_dim), device=dev)
+    stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev)
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_gather(torch, wl, bank, inp, live, args.cpu_seconds, cfg_name)
+    K = args.steps if args.steps is not None else 20
+
+    def launch_one(i):
+        sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+                   idx1=inp["idx1"], w1=inp["w1"], out0=out0, out1=out1, stash=stash)
+
+    ms = _run_steps(torch, args, launch_one, K)
+    ms_step = ms / K
+    row_bytes = live * (wl.width0 + wl.width1) * wl.head_dim * es + T * wl.width0 * wl.head_dim * es
+    gbps = row_bytes / (ms_step * 1e-3) / 1e9
+    config = {"workload": f"{cfg_name}: {wl.name}", "tokens": T, "live_tokens": live, "chunk": wl.chunk,
+              "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1], "slots": wl.num_slots,
+              "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "launch": args.launch, "seed": args.seed}
+    value = T * K / (ms * 1e-3)
+    return dict(value=value, unit="tokens/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
+                row_bytes=row_bytes, kernel="sdm_gather_kernel", cpu=cpu, tokens_per_s=value)
+
+
+def calibrate_copy(torch):
+    """A plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB), for counter scaling."""
+    dev = torch.device("cuda", 0)
+    n = (1 << 30) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty(n, device=dev)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    ms = _timed(torch, torch.cuda.current_stream(), lambda: torch.mul(src, 1.0, out=dst))
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
+                      "gbps": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); a step is one GPU's share of streams or tokens, which needs no exchange.",
+              file=sys.stderr, flush=True)
+        return 2
+    sys.path.insert(0, ROOT)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return 0
+    import gen
+    wl = gen.WORKLOADS[args.config]
+    if isinstance(wl, gen.DecodeWorkload):
+        r = bench_decode(torch, args, args.config, wl)
+    else:
+        r = bench_gather(torch, args, args.config, wl)
+    traffic = stored_traffic(args.config)
+    out = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": r["unit"],
+        "n_gpus": 1,
+        "steps": r["K"],
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; gen/workloads.py)",
+        "config": r["config"],
+        "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": r["kernel"], "algorithmic_bytes_per_launch": r["row_bytes"]},
+        "cpu_baseline": r["cpu"],
+        "tokens_per_s": r["tokens_per_s"],
+        "row_gbps": r["gbps"],
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * libsdm: the sparse-delta-memory (SDM) decode step and token gather on an
+ * AMD Instinct MI355X (gfx950), behind a plain C ABI.
+ *
+ * Every pointer argument of a compute call is a DEVICE pointer to a contiguous,
+ * row-major array that the caller owns; the library allocates nothing, keeps
+ * no state between calls and only enqueues work on `hip_stream` (a
+ * hipStream_t; NULL = the null stream), so calls may be captured in a HIP
+ * graph. Results are ready when that stream reaches them. The cheap argument
+ * checks run on the host before any HIP call; a failing call enqueues nothing
+ * and returns one of the status codes below, with a message for
+ * sdm_last_error() on the calling thread.
+ *
+ * Setting the environment variable SDM_DEBUG_VALIDATE=1 adds checks that need
+ * the slot lists on the host (bounds, distinct write slots, private stream
+ * ranges, per-chunk valid counts): each call then copies them from the device
+ * and synchronises `hip_stream`. Without it those preconditions are not
+ * checked, and a call that breaks them has undefined results.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDM_ABI_VERSION 1
+#define SDM_MAX_WIDTH 256 /* largest W, R and gather width */
+
+/* Element types (sdm_dtype). */
+enum {
+    SDM_F32 = 0,  /* IEEE float32 */
+    SDM_BF16 = 1, /* bfloat16: the high 16 bits of a float32 */
+    SDM_I32 = 2,
+    SDM_I64 = 3
+};
+
+/* Status codes (sdm_status). */
+enum {
+    SDM_OK = 0,
+    SDM_E_DTYPE = 1,   /* an element type outside the ones an argument accepts */
+    SDM_E_SHAPE = 2,   /* a size that is negative, zero where one is needed, or inconsistent */
+    SDM_E_RANGE = 3,   /* a width outside 1..SDM_MAX_WIDTH, a count outside its range, or a
+                          slot-list precondition broken (SDM_DEBUG_VALIDATE only) */
+    SDM_E_ALIGN = 4,   /* a pointer not aligned to its element size */
+    SDM_E_OVERLAP = 5, /* an output overlapping the bank or another output */
+    SDM_E_NULL = 6,    /* a required pointer is NULL (or operand 1 given in part) */
+    SDM_E_DEVICE = 7,  /* no HIP device, or a pointer that is not device memory
+                          (SDM_DEBUG_VALIDATE only) */
+    SDM_E_HIP = 8      /* the HIP runtime reported an error; see sdm_last_error() */
+};
+
+/*
+ * sdm_decode_step: advance every stream by one token, then read the bank back.
+ *
+ * Operation (page "sparse_delta_memory/decode.py", docstring of
+ * sdm_decode_step; prior art: _sdm_decode_kernel on the same page). For each
+ * stream s, with d[w] = exp(g[s, G == 1 ? 0 : w]):
+ *     retrieved = sum_w k_val[s,w] d[w] bank[k_idx[s,w]]
+ *     delta_v   = beta[s] (v[s] - retrieved)
+ *     bank[k_idx[s,w]] = d[w] bank[k_idx[s,w]] + k_val[s,w] delta_v   for each w
+ *     readings[s] = sum_r q_val[s,r] bank[q_idx[s,r]]                  after the writes
+ * Only the W written rows change (decay is applied to them alone). k_val, v and
+ * q_val are rounded to the bank dtype (round to nearest even) before use; beta
+ * and g are float32; arithmetic is float32; rows are stored and readings
+ * returned in the bank dtype (rounded to nearest even). d[w] is the float32
+ * nearest to exp(g) (computed in double).
+ *
+ * Summation order (fixed, a function of W and R only): with
+ *     RG = min(32, next_pow2(ceil(max(W, R) / 8)))
+ * each column's retrieved is ((0 + p_0) + p_1) + ... + p_{RG-1}, where p_j is
+ * the fused multiply-add chain over w = j, j + RG, j + 2 RG, ... ascending,
+ * starting from +0, of (k_val[w] d[w]) * row_w (the product k_val[w] d[w]
+ * rounded to float32 first); readings use the same scheme over r with q_val.
+ * Each new row element is fma(k_val[w], delta_v, row * d[w]) with row * d[w]
+ * rounded first, and delta_v = beta * (v - retrieved) with two roundings.
+ * Results do not depend on the GPU's size or on which other streams are in the
+ * call.
+ *
+ * Arguments:
+ *   bank        [num_slots, head_dim] of bank_dtype (SDM_F32 or SDM_BF16);
+ *               read and written in place.
+ *   num_slots   >= 1. head_dim >= 1.
+ *   streams     >= 0; 0 enqueues nothing and returns SDM_OK.
+ *   W, R        write and read widths, 1..SDM_MAX_WIDTH.
+ *   G           1 (one gate per stream) or W (one gate per write).
+ *   k_idx       [streams, W] absolute bank rows, SDM_I32 or SDM_I64 (k_idx_dtype).
+ *   k_val       [streams, W], v [streams, head_dim], q_val [streams, R], all of
+ *               val_dtype (SDM_F32 or SDM_BF16).
+ *   beta        [streams] float32.  g [streams, G] float32.
+ *   q_idx       [streams, R] absolute bank rows, SDM_I32 or SDM_I64 (q_idx_dtype;
+ *               may differ from k_idx_dtype).
+ *   readings    [streams, head_dim] of bank_dtype, written; must not overlap bank.
+ * Preconditions (checked only under SDM_DEBUG_VALIDATE): every slot is in
+ * [0, num_slots); a stream's W write slots are distinct; the slots a stream
+ * touches (written or read) belong to no other stream of the call. Read slots
+ * may repeat (each occurrence adds its term) and may coincide with write slots
+ * (the read sees the new row).
+ * Errors: SDM_E_DTYPE, SDM_E_SHAPE, SDM_E_RANGE, SDM_E_NULL, SDM_E_ALIGN,
+ * SDM_E_OVERLAP (readings and bank overlap), SDM_E_HIP (launch failure).
+ */
+int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                    int64_t streams, int32_t W, int32_t R, int32_t G,
+                    const void* k_idx, int k_idx_dtype,
+                    const void* k_val, const void* v, const void* q_val, int val_dtype,
+                    const float* beta, const float* g,
+                    const void* q_idx, int q_idx_dtype,
+                    void* readings, void* hip_stream);
+
+/*
+ * sdm_gather: per-token weighted sums of bank rows, with a raw copy of the rows.
+ *
+ * Operation (page "sparse_delta_memory/cuda/gather_cuda.py", module docstring;
+ * prior art: token_gather_kernel on the same page). For each token t of the
+ * call and each operand o (operand 1 is optional):
+ *     out_o[t]    = sum_n w_o[t,n] bank[idx_o[t,n]]      (float32 accumulation)
+ *     stash[t, n] = bank[idx_0[t,n]]                     (raw bits, n < width0)
+ * Token t is padding when (t mod chunk) >= limit, where limit = chunk_valid[t /
+ * chunk] if chunk_valid is given, else valid: a padding token reads no slot or
+ * weight and writes +0.0 outputs and all-zero stash rows. Weights are used as
+ * given (a bfloat16 weight is widened exactly, not rounded to the bank dtype).
+ *
+ * Summation order (fixed): each output element is one fused multiply-add
+ * chain over n = 0, 1, ..., width-1 ascending, starting from +0 (the "groups =
+ * 1" order of the pages); it depends on nothing but the inputs.
+ *
+ * Arguments:
+ *   bank         [num_slots, head_dim] of bank_dtype (SDM_F32 or SDM_BF16); read only.
+ *   tokens       >= 0, a multiple of chunk; 0 enqueues nothing and returns SDM_OK.
+ *   chunk        >= 1.  valid in [0, chunk].
+ *   chunk_valid  NULL, or [tokens / chunk] int32 on the device, each in [0, chunk]
+ *                (checked only under SDM_DEBUG_VALIDATE); overrides valid.
+ *   idx_dtype    SDM_I32 or SDM_I64, for both operands.  w_dtype SDM_F32 or SDM_BF16.
+ *   idx0, w0     [tokens, width0]; width0 in 1..SDM_MAX_WIDTH.  out0 [tokens, head_dim] float32.
+ *   stash        NULL (no copy), or [tokens, width0, head_dim] of bank_dtype.
+ *   idx1, w1, out1, width1: the second operand, like the first; all NULL with
+ *                width1 = 0 for one operand, or all given with width1 in 1..SDM_MAX_WIDTH.
+ * Slots must lie in [0, num_slots) (checked only under SDM_DEBUG_VALIDATE).
+ * Outputs and stash must not overlap the bank or one another (SDM_E_OVERLAP).
+ * Errors: SDM_E_DTYPE, SDM_E_SHAPE, SDM_E_RANGE, SDM_E_NULL, SDM_E_ALIGN,
+ * SDM_E_OVERLAP, SDM_E_HIP.
+ */
+int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+               int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid,
+               int idx_dtype, int w_dtype,
+               const void* idx0, const void* w0, int32_t width0, float* out0, void* stash,
+               const void* idx1, const void* w1, int32_t width1, float* out1,
+               void* hip_stream);
+
+/* Message of the last failing call on this thread ("" if none). The pointer stays
+ * valid until the next libsdm call on the same thread. */
+const char* sdm_last_error(void);
+
+/* SDM_ABI_VERSION of the library. */
+int sdm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,24 @@
+"""sparse_delta_rule_amd: the sparse-delta-memory decode step and token gather on MI355X.
+
+The compute lives in ``libsdm.so`` (hand-written HIP kernels for gfx950 behind
+the C ABI declared in ``include/sdm.h``). This package only marshals torch
+tensors (device memory and streams) into those calls: it has no fallback, and
+every entry point raises if the library is not built or a call fails.
+
+    readings = sdm_decode_step(bank, k_idx, k_val, v, beta, g, q_idx, q_val)
+    out0, stash, out1 = sdm_gather(bank, idx0, w0, chunk=64, valid=64, idx1=..., w1=...)
+"""
+
+from ._binding import (  # noqa: F401
+    SDM_BF16,
+    SDM_F32,
+    SDM_I32,
+    SDM_I64,
+    SDM_MAX_WIDTH,
+    SdmError,
+    abi_version,
+    library,
+    library_path,
+    sdm_decode_step,
+    sdm_gather,
+)

@@ -1,0 +1,188 @@
+"""ctypes binding of libsdm (include/sdm.h): argument marshalling only.
+
+Tensors must be CUDA (HIP) tensors on one device and contiguous; the work is
+enqueued on torch's current stream of that device, so it orders with the
+surrounding torch work and can be captured in a torch.cuda.CUDAGraph.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+SDM_F32, SDM_BF16, SDM_I32, SDM_I64 = 0, 1, 2, 3
+SDM_MAX_WIDTH = 256
+
+_STATUS = {1: "SDM_E_DTYPE", 2: "SDM_E_SHAPE", 3: "SDM_E_RANGE", 4: "SDM_E_ALIGN",
+           5: "SDM_E_OVERLAP", 6: "SDM_E_NULL", 7: "SDM_E_DEVICE", 8: "SDM_E_HIP"}
+
+_DTYPES = {torch.float32: SDM_F32, torch.bfloat16: SDM_BF16, torch.int32: SDM_I32,
+           torch.int64: SDM_I64}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("SDM_LIBRARY", os.path.join(_HERE, "libsdm.so"))
+
+
+class SdmError(RuntimeError):
+    """A libsdm call returned a status other than SDM_OK."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libsdm, with argument types declared (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libsdm is not built ({path} is missing); run "
+                           "`python -m sparse_delta_rule_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.sdm_decode_step.argtypes = [P, i32, i64, i64, i64, i32, i32, i32, P, i32, P, P, P, i32,
+                                    P, P, P, i32, P, P]
+    lib.sdm_decode_step.restype = ctypes.c_int
+    lib.sdm_gather.argtypes = [P, i32, i64, i64, i64, i64, i64, P, i32, i32, P, P, i32, P, P,
+                               P, P, i32, P, P]
+    lib.sdm_gather.restype = ctypes.c_int
+    lib.sdm_last_error.argtypes = []
+    lib.sdm_last_error.restype = ctypes.c_char_p
+    lib.sdm_abi_version.argtypes = []
+    lib.sdm_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(library().sdm_abi_version())
+
+
+def _raise(status: int):
+    msg = library().sdm_last_error().decode(errors="replace")
+    raise SdmError(status, msg)
+
+
+def _dt(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what} has unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_check(device: torch.device, **tensors):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the bank on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def sdm_decode_step(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
+                    beta: torch.Tensor, g: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor,
+                    readings: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step for every stream (``sdm_decode_step`` of include/sdm.h).
+
+    bank [num_slots, head_dim] (float32 or bfloat16) is updated in place;
+    k_idx, k_val [..., W]; v [..., head_dim]; beta [..., 1]; g [..., 1] or [..., W];
+    q_idx, q_val [..., R]; all with the same leading dims (one entry per stream).
+    k_val, v and q_val share one dtype (float32 or bfloat16); beta and g are float32.
+    Returns readings shaped like ``v`` in the bank dtype (``readings`` if given).
+    """
+    if bank.dim() != 2:
+        raise ValueError("bank must be [num_slots, head_dim]")
+    hd = bank.shape[1]
+    W, R, G = k_idx.shape[-1], q_idx.shape[-1], g.shape[-1]
+    lead = tuple(k_idx.shape[:-1])
+    for name, t, n in (("k_val", k_val, W), ("v", v, hd), ("beta", beta, 1), ("g", g, G),
+                       ("q_idx", q_idx, R), ("q_val", q_val, R)):
+        if tuple(t.shape) != lead + (n,):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {lead + (n,)}")
+    if not (k_val.dtype == v.dtype == q_val.dtype):
+        raise TypeError("k_val, v and q_val must share one dtype")
+    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+        raise TypeError("beta and g must be float32")
+    if readings is None:
+        readings = torch.empty(v.shape, dtype=bank.dtype, device=bank.device)
+    elif tuple(readings.shape) != tuple(v.shape) or readings.dtype != bank.dtype:
+        raise ValueError("readings must be shaped like v, in the bank dtype")
+    _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
+               q_val=q_val, readings=readings)
+    streams = k_idx.numel() // W
+    rc = library().sdm_decode_step(
+        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, streams, W, R, G,
+        _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
+        _ptr(beta), _ptr(g), _ptr(q_idx), _dt(q_idx, "q_idx"), _ptr(readings),
+        _stream_handle(bank.device))
+    if rc != 0:
+        _raise(rc)
+    return readings
+
+
+def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chunk: int,
+               valid: Optional[int] = None, chunk_valid: Optional[torch.Tensor] = None,
+               idx1: Optional[torch.Tensor] = None, w1: Optional[torch.Tensor] = None,
+               out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None,
+               stash: Optional[torch.Tensor] = None, with_stash: bool = True):
+    """Token gather (``sdm_gather`` of include/sdm.h). Returns (out0, stash, out1).
+
+    idx0, w0 [tokens, width0] (idx int32 or int64, weights float32 or bfloat16);
+    optional second operand idx1, w1 [tokens, width1]. ``valid`` defaults to
+    ``chunk``; ``chunk_valid`` (int32 [tokens / chunk]) overrides it per chunk.
+    out0/out1 [tokens, head_dim] float32 and stash [tokens, width0, head_dim] in the
+    bank dtype are allocated when not given (no stash if ``with_stash`` is False).
+    """
+    if bank.dim() != 2 or idx0.dim() != 2 or tuple(w0.shape) != tuple(idx0.shape):
+        raise ValueError("bank [slots, hd], idx0 and w0 [tokens, width0] expected")
+    tokens, W0 = idx0.shape
+    hd = bank.shape[1]
+    dev = bank.device
+    two = idx1 is not None
+    if two != (w1 is not None):
+        raise ValueError("idx1 and w1 go together")
+    W1 = 0
+    if two:
+        if idx1.dim() != 2 or tuple(w1.shape) != tuple(idx1.shape) or idx1.shape[0] != tokens:
+            raise ValueError("idx1 and w1 must be [tokens, width1]")
+        W1 = idx1.shape[1]
+        if idx1.dtype != idx0.dtype or w1.dtype != w0.dtype:
+            raise TypeError("both operands must share index and weight dtypes")
+    if out0 is None:
+        out0 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
+    if two and out1 is None:
+        out1 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
+    if stash is None and with_stash:
+        stash = torch.empty((tokens, W0, hd), dtype=bank.dtype, device=dev)
+    if chunk_valid is not None and chunk_valid.dtype != torch.int32:
+        raise TypeError("chunk_valid must be int32")
+    _dev_check(dev, bank=bank, idx0=idx0, w0=w0, out0=out0, stash=stash, chunk_valid=chunk_valid,
+               idx1=idx1, w1=w1, out1=out1)
+    rc = library().sdm_gather(
+        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, tokens, chunk,
+        chunk if valid is None else valid, _ptr(chunk_valid), _dt(idx0, "idx0"), _dt(w0, "w0"),
+        _ptr(idx0), _ptr(w0), W0, _ptr(out0), _ptr(stash), _ptr(idx1), _ptr(w1), W1,
+        _ptr(out1), _stream_handle(dev))
+    if rc != 0:
+        _raise(rc)
+    return out0, stash, out1

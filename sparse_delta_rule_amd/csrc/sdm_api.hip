@@ -1,0 +1,344 @@
+// The libsdm C ABI: argument checks, error reporting and kernel launches.
+//
+// The checks follow the argument contracts the pages state for the decode
+// step (page "sparse_delta_memory/decode.py", sdm_decode_step) and the token
+// gather (page "sparse_delta_memory/cuda/gather_cuda.py", token_gather and its
+// host checks), reported as status codes with a thread-local message instead of
+// exceptions. Everything cheap is checked on the host before the first HIP call.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/sdm.h"
+#include "sdm_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return SDM_OK;
+}
+
+int elem_size(int dtype) {
+    switch (dtype) {
+        case SDM_F32: return 4;
+        case SDM_BF16: return 2;
+        case SDM_I32: return 4;
+        case SDM_I64: return 8;
+        default: return 0;
+    }
+}
+
+bool aligned(const void* p, int bytes) { return reinterpret_cast<uintptr_t>(p) % uintptr_t(bytes) == 0; }
+
+// Half-open byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + uintptr_t(nb) && y < x + uintptr_t(na);
+}
+
+// a * b * c fits in int64 (all non-negative).
+bool mul_fits(int64_t a, int64_t b, int64_t c = 1) {
+    const int64_t lim = INT64_MAX;
+    if (a == 0 || b == 0 || c == 0) return true;
+    if (a > lim / b) return false;
+    return a * b <= lim / c;
+}
+
+bool debug_validate() {
+    static const int on = [] {
+        const char* e = std::getenv("SDM_DEBUG_VALIDATE");
+        return (e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0) ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+int check_device_ptr(const void* p, const char* name) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_E_DEVICE, "%s is not a HIP device pointer (%s)", name, hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(SDM_E_DEVICE, "%s is not device memory", name);
+    return SDM_OK;
+}
+
+// Copy a device slot list to the host as int64.
+int fetch_slots(const void* dev, int dtype, int64_t n, std::vector<int64_t>& out, hipStream_t stream,
+                const char* name) {
+    out.assign(size_t(n), 0);
+    if (n == 0) return SDM_OK;
+    hipError_t e;
+    if (dtype == SDM_I64) {
+        e = hipMemcpyAsync(out.data(), dev, size_t(n) * 8, hipMemcpyDeviceToHost, stream);
+    } else {
+        std::vector<int32_t> tmp(static_cast<size_t>(n));
+        e = hipMemcpyAsync(tmp.data(), dev, size_t(n) * 4, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        for (int64_t i = 0; i < n; ++i) out[size_t(i)] = tmp[size_t(i)];
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "copying %s to the host: %s", name, hipGetErrorString(e));
+    return SDM_OK;
+}
+
+int validate_decode_slots(int64_t num_slots, int64_t streams, int W, int R, const void* k_idx, int kd,
+                          const void* q_idx, int qd, hipStream_t stream) {
+    std::vector<int64_t> k, q;
+    int rc = fetch_slots(k_idx, kd, streams * W, k, stream, "k_idx");
+    if (rc != SDM_OK) return rc;
+    rc = fetch_slots(q_idx, qd, streams * R, q, stream, "q_idx");
+    if (rc != SDM_OK) return rc;
+    std::unordered_map<int64_t, int64_t> owner;
+    owner.reserve(size_t(streams) * size_t(W + R));
+    for (int64_t s = 0; s < streams; ++s) {
+        for (int w = 0; w < W; ++w) {
+            const int64_t x = k[size_t(s * W + w)];
+            if (x < 0 || x >= num_slots)
+                return fail(SDM_E_RANGE, "k_idx[%lld, %d] = %lld outside [0, %lld)", (long long)s, w,
+                            (long long)x, (long long)num_slots);
+            for (int u = 0; u < w; ++u)
+                if (k[size_t(s * W + u)] == x)
+                    return fail(SDM_E_RANGE, "stream %lld writes slot %lld twice", (long long)s, (long long)x);
+        }
+        for (int r = 0; r < R; ++r) {
+            const int64_t x = q[size_t(s * R + r)];
+            if (x < 0 || x >= num_slots)
+                return fail(SDM_E_RANGE, "q_idx[%lld, %d] = %lld outside [0, %lld)", (long long)s, r,
+                            (long long)x, (long long)num_slots);
+        }
+        for (int i = 0; i < W + R; ++i) {
+            const int64_t x = i < W ? k[size_t(s * W + i)] : q[size_t(s * R + i - W)];
+            auto it = owner.emplace(x, s);
+            if (!it.second && it.first->second != s)
+                return fail(SDM_E_RANGE, "slot %lld is used by streams %lld and %lld", (long long)x,
+                            (long long)it.first->second, (long long)s);
+        }
+    }
+    return SDM_OK;
+}
+
+int validate_gather_slots(int64_t num_slots, int64_t tokens, int64_t chunk, const int32_t* chunk_valid,
+                          const void* idx, int width, int idx_dtype, hipStream_t stream, const char* name) {
+    std::vector<int64_t> v;
+    int rc = fetch_slots(idx, idx_dtype, tokens * width, v, stream, name);
+    if (rc != SDM_OK) return rc;
+    for (int64_t i = 0; i < tokens * width; ++i)
+        if (v[size_t(i)] < 0 || v[size_t(i)] >= num_slots)
+            return fail(SDM_E_RANGE, "%s[%lld] = %lld outside [0, %lld)", name, (long long)i,
+                        (long long)v[size_t(i)], (long long)num_slots);
+    if (chunk_valid != nullptr) {
+        const int64_t chunks = tokens / chunk;
+        std::vector<int32_t> cv(static_cast<size_t>(chunks));
+        hipError_t e = hipMemcpyAsync(cv.data(), chunk_valid, size_t(chunks) * 4, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(SDM_E_HIP, "copying chunk_valid: %s", hipGetErrorString(e));
+        for (int64_t c = 0; c < chunks; ++c)
+            if (cv[size_t(c)] < 0 || cv[size_t(c)] > chunk)
+                return fail(SDM_E_RANGE, "chunk_valid[%lld] = %d outside [0, %lld]", (long long)c, cv[size_t(c)],
+                            (long long)chunk);
+    }
+    return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdm_last_error(void) { return g_last_error.c_str(); }
+
+int sdm_abi_version(void) { return SDM_ABI_VERSION; }
+
+int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t streams,
+                    int32_t W, int32_t R, int32_t G, const void* k_idx, int k_idx_dtype, const void* k_val,
+                    const void* v, const void* q_val, int val_dtype, const float* beta, const float* g,
+                    const void* q_idx, int q_idx_dtype, void* readings, void* hip_stream) {
+    if (bank_dtype != SDM_F32 && bank_dtype != SDM_BF16)
+        return fail(SDM_E_DTYPE, "sdm_decode_step: bank must be float32 or bfloat16 (dtype %d)", bank_dtype);
+    if (val_dtype != SDM_F32 && val_dtype != SDM_BF16)
+        return fail(SDM_E_DTYPE, "sdm_decode_step: k_val, v, q_val must be float32 or bfloat16 (dtype %d)",
+                    val_dtype);
+    if ((k_idx_dtype != SDM_I32 && k_idx_dtype != SDM_I64) || (q_idx_dtype != SDM_I32 && q_idx_dtype != SDM_I64))
+        return fail(SDM_E_DTYPE, "sdm_decode_step: k_idx and q_idx must be int32 or int64 (dtypes %d, %d)",
+                    k_idx_dtype, q_idx_dtype);
+    if (num_slots < 1 || head_dim < 1)
+        return fail(SDM_E_SHAPE, "sdm_decode_step: the bank needs at least one slot and one column, got [%lld, %lld]",
+                    (long long)num_slots, (long long)head_dim);
+    if (streams < 0) return fail(SDM_E_SHAPE, "sdm_decode_step: streams = %lld < 0", (long long)streams);
+    if (W < 1 || W > SDM_MAX_WIDTH || R < 1 || R > SDM_MAX_WIDTH)
+        return fail(SDM_E_RANGE, "sdm_decode_step: W and R must be in 1..%d, got W=%d, R=%d", SDM_MAX_WIDTH, W, R);
+    if (G != 1 && G != W)
+        return fail(SDM_E_SHAPE, "sdm_decode_step: G must be 1 or W=%d, got %d", W, G);
+    const int es = elem_size(bank_dtype);
+    if (!mul_fits(num_slots, head_dim, es) || !mul_fits(streams, head_dim, es) || !mul_fits(streams, SDM_MAX_WIDTH, 8))
+        return fail(SDM_E_SHAPE, "sdm_decode_step: sizes overflow 64-bit byte counts");
+    if (streams > 0x7fffffffLL)
+        return fail(SDM_E_SHAPE, "sdm_decode_step: at most 2^31-1 streams per call, got %lld", (long long)streams);
+    if (streams == 0) return ok();
+    const struct { const void* p; const char* name; } req[] = {
+        {bank, "bank"}, {k_idx, "k_idx"}, {k_val, "k_val"}, {v, "v"}, {q_val, "q_val"},
+        {beta, "beta"}, {g, "g"}, {q_idx, "q_idx"}, {readings, "readings"}};
+    for (const auto& r : req)
+        if (r.p == nullptr) return fail(SDM_E_NULL, "sdm_decode_step: %s is NULL", r.name);
+    const int vs = elem_size(val_dtype);
+    if (!aligned(bank, es) || !aligned(readings, es) || !aligned(k_idx, elem_size(k_idx_dtype)) ||
+        !aligned(q_idx, elem_size(q_idx_dtype)) || !aligned(k_val, vs) || !aligned(v, vs) || !aligned(q_val, vs) ||
+        !aligned(beta, 4) || !aligned(g, 4))
+        return fail(SDM_E_ALIGN, "sdm_decode_step: a pointer is not aligned to its element size");
+    if (overlap(readings, streams * head_dim * es, bank, num_slots * head_dim * es))
+        return fail(SDM_E_OVERLAP, "sdm_decode_step: readings overlap the bank");
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (debug_validate()) {
+        for (const auto& r : req) {
+            int rc = check_device_ptr(r.p, r.name);
+            if (rc != SDM_OK) return rc;
+        }
+        int rc = validate_decode_slots(num_slots, streams, W, R, k_idx, k_idx_dtype, q_idx, q_idx_dtype, stream);
+        if (rc != SDM_OK) return rc;
+    }
+
+    const sdm::DecodeGeometry geo =
+        sdm::decode_geometry(es, head_dim, W, R, reinterpret_cast<uintptr_t>(bank));
+    if (geo.slices > 65535)
+        return fail(SDM_E_SHAPE, "sdm_decode_step: head_dim %lld needs %d column slices (max 65535)",
+                    (long long)head_dim, geo.slices);
+    sdm::DecodeParams p{};
+    p.bank = bank;
+    p.k_idx = k_idx;
+    p.q_idx = q_idx;
+    p.k_val = k_val;
+    p.v = v;
+    p.q_val = q_val;
+    p.beta = beta;
+    p.g = g;
+    p.readings = readings;
+    p.hd = head_dim;
+    p.W = W;
+    p.R = R;
+    p.G = G;
+    p.vpr = geo.vpr;
+    p.lpr = geo.lpr;
+    p.rg = geo.rg;
+    p.k64 = k_idx_dtype == SDM_I64;
+    p.q64 = q_idx_dtype == SDM_I64;
+    p.val_bf16 = val_dtype == SDM_BF16;
+    hipError_t e = sdm::launch_decode(p, geo, streams, bank_dtype == SDM_BF16, stream);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "sdm_decode_step: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t tokens, int64_t chunk,
+               int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype, const void* idx0,
+               const void* w0, int32_t width0, float* out0, void* stash, const void* idx1, const void* w1,
+               int32_t width1, float* out1, void* hip_stream) {
+    if (bank_dtype != SDM_F32 && bank_dtype != SDM_BF16)
+        return fail(SDM_E_DTYPE, "sdm_gather: bank must be float32 or bfloat16 (dtype %d)", bank_dtype);
+    if (idx_dtype != SDM_I32 && idx_dtype != SDM_I64)
+        return fail(SDM_E_DTYPE, "sdm_gather: indices must be int32 or int64 (dtype %d)", idx_dtype);
+    if (w_dtype != SDM_F32 && w_dtype != SDM_BF16)
+        return fail(SDM_E_DTYPE, "sdm_gather: weights must be float32 or bfloat16 (dtype %d)", w_dtype);
+    if (num_slots < 1 || head_dim < 1)
+        return fail(SDM_E_SHAPE, "sdm_gather: the bank needs at least one slot and one column, got [%lld, %lld]",
+                    (long long)num_slots, (long long)head_dim);
+    if (tokens < 0 || chunk < 1 || tokens % chunk != 0 || valid < 0 || valid > chunk)
+        return fail(SDM_E_SHAPE, "sdm_gather: need tokens = k * chunk and 0 <= valid <= chunk, got tokens=%lld "
+                    "chunk=%lld valid=%lld", (long long)tokens, (long long)chunk, (long long)valid);
+    if (width0 < 1 || width0 > SDM_MAX_WIDTH)
+        return fail(SDM_E_RANGE, "sdm_gather: width0 must be in 1..%d, got %d", SDM_MAX_WIDTH, width0);
+    const bool two = idx1 != nullptr || w1 != nullptr || out1 != nullptr || width1 != 0;
+    if (two) {
+        if (idx1 == nullptr || w1 == nullptr || out1 == nullptr)
+            return fail(SDM_E_NULL, "sdm_gather: idx1, w1 and out1 go together");
+        if (width1 < 1 || width1 > SDM_MAX_WIDTH)
+            return fail(SDM_E_RANGE, "sdm_gather: width1 must be in 1..%d, got %d", SDM_MAX_WIDTH, width1);
+    }
+    const int es = elem_size(bank_dtype);
+    if (!mul_fits(num_slots, head_dim, es) || !mul_fits(tokens, SDM_MAX_WIDTH, head_dim * 8))
+        return fail(SDM_E_SHAPE, "sdm_gather: sizes overflow 64-bit byte counts");
+    if (tokens == 0) return ok();
+    if (bank == nullptr || idx0 == nullptr || w0 == nullptr || out0 == nullptr)
+        return fail(SDM_E_NULL, "sdm_gather: bank, idx0, w0 and out0 are required");
+    const int is = elem_size(idx_dtype), ws = elem_size(w_dtype);
+    if (!aligned(bank, es) || !aligned(idx0, is) || !aligned(w0, ws) || !aligned(out0, 4) ||
+        (stash != nullptr && !aligned(stash, es)) || !aligned(chunk_valid, 4) ||
+        (two && (!aligned(idx1, is) || !aligned(w1, ws) || !aligned(out1, 4))))
+        return fail(SDM_E_ALIGN, "sdm_gather: a pointer is not aligned to its element size");
+    const int64_t bank_bytes = num_slots * head_dim * es;
+    const int64_t out_bytes = tokens * head_dim * 4;
+    const int64_t stash_bytes = stash != nullptr ? tokens * width0 * head_dim * es : 0;
+    if (overlap(out0, out_bytes, bank, bank_bytes) || overlap(stash, stash_bytes, bank, bank_bytes) ||
+        (two && overlap(out1, out_bytes, bank, bank_bytes)))
+        return fail(SDM_E_OVERLAP, "sdm_gather: stash and outputs must not overlap the bank");
+    if (overlap(out0, out_bytes, stash, stash_bytes) || (two && (overlap(out1, out_bytes, stash, stash_bytes) ||
+                                                                 overlap(out0, out_bytes, out1, out_bytes))))
+        return fail(SDM_E_OVERLAP, "sdm_gather: stash and outputs must not overlap one another");
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (debug_validate()) {
+        const void* ptrs[] = {bank, idx0, w0, out0, stash, chunk_valid, idx1, w1, out1};
+        const char* names[] = {"bank", "idx0", "w0", "out0", "stash", "chunk_valid", "idx1", "w1", "out1"};
+        for (int i = 0; i < 9; ++i) {
+            if (ptrs[i] == nullptr) continue;
+            int rc = check_device_ptr(ptrs[i], names[i]);
+            if (rc != SDM_OK) return rc;
+        }
+        int rc = validate_gather_slots(num_slots, tokens, chunk, chunk_valid, idx0, width0, idx_dtype, stream, "idx0");
+        if (rc == SDM_OK && two)
+            rc = validate_gather_slots(num_slots, tokens, chunk, nullptr, idx1, width1, idx_dtype, stream, "idx1");
+        if (rc != SDM_OK) return rc;
+    }
+
+    const sdm::GatherGeometry geo = sdm::gather_geometry(es, head_dim, reinterpret_cast<uintptr_t>(bank),
+                                                         reinterpret_cast<uintptr_t>(stash));
+    const int64_t blocks = (tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
+    if (blocks > 0x7fffffffLL || geo.slices > 65535)
+        return fail(SDM_E_SHAPE, "sdm_gather: %lld tokens x %d column slices exceed the grid", (long long)tokens,
+                    geo.slices);
+    sdm::GatherParams p{};
+    p.bank = bank;
+    p.stash = stash;
+    p.idx0 = idx0;
+    p.w0 = w0;
+    p.out0 = out0;
+    p.idx1 = two ? idx1 : nullptr;
+    p.w1 = two ? w1 : nullptr;
+    p.out1 = two ? out1 : nullptr;
+    p.chunk_valid = chunk_valid;
+    p.hd = head_dim;
+    p.tokens = tokens;
+    p.chunk = chunk;
+    p.valid = valid;
+    p.width0 = width0;
+    p.width1 = two ? width1 : 0;
+    p.vpr = geo.vpr;
+    p.lpr = geo.lpr;
+    p.idx64 = idx_dtype == SDM_I64;
+    p.w_bf16 = w_dtype == SDM_BF16;
+    p.out_vec = aligned(out0, 16) && (!two || aligned(out1, 16));
+    hipError_t e = sdm::launch_gather(p, geo, bank_dtype == SDM_BF16, two, stream);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "sdm_gather: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations of the libsdm HIP path: launch parameter blocks, the
+// element helpers the kernels share, and the launchers the C ABI calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+constexpr int kMaxWidth = 256;
+
+// ------------------------------------------------------------------ elements
+// A bank element is kept as its raw bits: uint16_t for bfloat16, float for float32.
+template <int VB> struct RawVec;
+template <> struct RawVec<16> { using T = uint4; };
+template <> struct RawVec<8> { using T = uint2; };
+template <> struct RawVec<4> { using T = uint32_t; };
+template <> struct RawVec<2> { using T = uint16_t; };
+
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float widen(float f) { return f; }
+
+// float32 -> bfloat16 bits, round to nearest even: adding 0x7fff plus the kept
+// half's lowest bit carries into the kept half exactly when the dropped half is
+// above one half, or equal to it with an odd kept half. NaN stays a quiet NaN.
+// Branch-free (a select), so a wavefront never diverges on it.
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x40u;
+    return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);
+}
+
+template <typename E> __device__ __forceinline__ E narrow(float f);
+template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float f) { return to_bf16_rne(f); }
+template <> __device__ __forceinline__ float narrow<float>(float f) { return f; }
+
+// Round a float32 to the bank element type and widen it back.
+template <typename E> __device__ __forceinline__ float to_bank(float f) { return widen(narrow<E>(f)); }
+
+// A value or weight given as float32 or bfloat16.
+__device__ __forceinline__ float load_value(const void* p, int64_t i, bool bf16) {
+    return bf16 ? widen(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ int64_t load_slot(const void* p, int64_t i, bool i64) {
+    return i64 ? static_cast<const int64_t*>(p)[i] : int64_t(static_cast<const int32_t*>(p)[i]);
+}
+
+// ------------------------------------------------------------------ decode
+struct DecodeParams {
+    void* bank;
+    const void* k_idx;
+    const void* q_idx;
+    const void* k_val;
+    const void* v;
+    const void* q_val;
+    const float* beta;
+    const float* g;
+    void* readings;
+    int64_t hd;
+    int W, R, G;
+    int vpr;  // vectors per row
+    int lpr;  // lanes per row group: a power of two <= 32
+    int rg;   // row groups
+    int k64, q64, val_bf16;
+};
+
+struct DecodeGeometry {
+    int vb;      // bytes per vector load: 16, 8, 4 or 2
+    int vpr;     // vectors per row
+    int lpr;     // lanes per row group
+    int slices;  // column slices (grid y)
+    int rg;      // row groups: fixes the summation order
+    int jn;      // rows per lane per phase: 1, 2, 4 or 8
+    int threads; // lpr * rg
+    size_t lds;  // dynamic LDS bytes
+};
+
+DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr);
+hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, int64_t streams, bool bf16,
+                         hipStream_t stream);
+
+// ------------------------------------------------------------------ gather
+struct GatherParams {
+    const void* bank;
+    void* stash;
+    const void* idx0;
+    const void* w0;
+    float* out0;
+    const void* idx1;
+    const void* w1;
+    float* out1;
+    const int32_t* chunk_valid;
+    int64_t hd, tokens, chunk, valid;
+    int width0, width1;
+    int vpr;  // vectors per row
+    int lpr;  // lanes per token: a power of two <= 64
+    int idx64, w_bf16;
+    int out_vec;  // outputs aligned for whole-vector float stores
+};
+
+struct GatherGeometry {
+    int vb;
+    int vpr;
+    int lpr;
+    int slices;
+    int tokens_per_block;
+    int threads;
+};
+
+GatherGeometry gather_geometry(int es, int64_t hd, uintptr_t bank_addr, uintptr_t stash_addr);
+hipError_t launch_gather(const GatherParams& p, const GatherGeometry& geo, bool bf16, bool two,
+                         hipStream_t stream);
+
+}  // namespace sdm

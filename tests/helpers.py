@@ -92,3 +92,51 @@ def random_decode_case(rng: np.random.Generator, *, streams, slots_per_stream, h
         q_val=rng.standard_normal((S, R)).astype(np.float32),
     )
     return case
+
+
+# ----------------------------------------------------------------- GPU runs
+def documented_decode_groups(W: int, R: int) -> int:
+    """The decode's row-group count as include/sdm.h states it:
+    RG = min(32, next_pow2(ceil(max(W, R) / 8)))."""
+    need = -(-max(W, R) // 8)
+    rg = 1
+    while rg < need:
+        rg *= 2
+    return min(32, rg)
+
+
+def step_to_numpy(inp: dict) -> dict:
+    """One step's inputs as the oracle takes them (indices int64, values float32)."""
+    out = {}
+    for k, t in inp.items():
+        t = t.detach().cpu()
+        if k in ("k_idx", "q_idx"):
+            out[k] = t.to(torch.int64).numpy()
+        else:
+            out[k] = t.float().numpy()
+    return out
+
+
+def oracle_sequence(bank: np.ndarray, steps: list, groups: int):
+    """Run the oracle over a list of numpy step inputs; returns (bank, [readings])."""
+    import oracle
+    readings = []
+    for inp in steps:
+        readings.append(oracle.decode_step(bank, inp["k_idx"], inp["k_val"], inp["v"], inp["beta"],
+                                           inp["g"], inp["q_idx"], inp["q_val"], groups=groups))
+    return bank, readings
+
+
+def decode_tolerance_ok(x: np.ndarray, ref: np.ndarray, mag: np.ndarray, bf16: bool):
+    """The stated parity bar: |x - ref| <= 1e-5 max(|ref|, M) for a float32 bank,
+    <= ulp_bf16(ref) + 2^-8 max(|ref|, M) for a bfloat16 bank. Returns (ok, worst ratio)."""
+    x = widen(x).astype(np.float64)
+    ref = widen(ref).astype(np.float64)
+    scale = np.maximum(np.abs(ref), mag)
+    if bf16:
+        bound = ulp(ref, True) + 2.0 ** -8 * scale
+    else:
+        bound = 1e-5 * scale
+    err = np.abs(x - ref)
+    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1), np.where(err > 0, np.inf, 0))
+    return bool(np.all(err <= bound)), float(ratio.max(initial=0.0))

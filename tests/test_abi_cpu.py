@@ -1,0 +1,210 @@
+"""The C ABI without a GPU: the library loads, exports what include/sdm.h
+declares, and rejects bad arguments on the host before any HIP call.
+
+Every call here passes fake (never dereferenced) device addresses; each case
+is one that the host checks turn into a status code, so no kernel is launched.
+"""
+
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+import sparse_delta_rule_amd as sdm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+OK, E_DTYPE, E_SHAPE, E_RANGE, E_ALIGN, E_OVERLAP, E_NULL = 0, 1, 2, 3, 4, 5, 6
+F32, BF16, I32, I64 = 0, 1, 2, 3
+
+A = 0x10000000  # fake, 256-byte aligned device addresses, far apart
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_gather",
+                                     "sdm_last_error"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sdm.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    m = re.search(r"#define SDM_ABI_VERSION (\d+)", open(HEADER).read())
+    assert sdm.abi_version() == int(m.group(1))
+
+
+def test_constants_match_the_header():
+    text = open(HEADER).read()
+    for name in ("SDM_F32", "SDM_BF16", "SDM_I32", "SDM_I64"):
+        m = re.search(rf"\b{name} = (\d+)", text)
+        assert int(m.group(1)) == getattr(sdm, name)
+    m = re.search(r"#define SDM_MAX_WIDTH (\d+)", text)
+    assert int(m.group(1)) == sdm.SDM_MAX_WIDTH
+
+
+# ------------------------------------------------------------------ decode
+def decode_args(**kw):
+    a = dict(bank=A, bank_dtype=BF16, num_slots=1024, head_dim=128, streams=8, W=4, R=4, G=1,
+             k_idx=A + 1024 * MB, k_idx_dtype=I64, k_val=A + 1100 * MB, v=A + 1200 * MB,
+             q_val=A + 1300 * MB, val_dtype=F32, beta=A + 1400 * MB, g=A + 1500 * MB,
+             q_idx=A + 1600 * MB, q_idx_dtype=I32, readings=A + 1700 * MB, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_decode(**kw):
+    a = decode_args(**kw)
+    lib = sdm.library()
+    rc = lib.sdm_decode_step(a["bank"], a["bank_dtype"], a["num_slots"], a["head_dim"], a["streams"],
+                             a["W"], a["R"], a["G"], a["k_idx"], a["k_idx_dtype"], a["k_val"], a["v"],
+                             a["q_val"], a["val_dtype"], a["beta"], a["g"], a["q_idx"], a["q_idx_dtype"],
+                             a["readings"], a["stream"])
+    return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(bank_dtype=I32), E_DTYPE, "bank must be"),
+    (dict(bank_dtype=7), E_DTYPE, "bank must be"),
+    (dict(val_dtype=I64), E_DTYPE, "k_val, v, q_val"),
+    (dict(k_idx_dtype=F32), E_DTYPE, "k_idx and q_idx"),
+    (dict(q_idx_dtype=BF16), E_DTYPE, "k_idx and q_idx"),
+    (dict(num_slots=0), E_SHAPE, "at least one slot"),
+    (dict(head_dim=0), E_SHAPE, "at least one slot"),
+    (dict(streams=-1), E_SHAPE, "streams"),
+    (dict(W=0), E_RANGE, "W and R"),
+    (dict(W=257), E_RANGE, "W and R"),
+    (dict(R=0), E_RANGE, "W and R"),
+    (dict(R=300), E_RANGE, "W and R"),
+    (dict(G=2), E_SHAPE, "G must be 1 or W"),
+    (dict(W=4, G=5), E_SHAPE, "G must be 1 or W"),
+    (dict(bank=None), E_NULL, "bank is NULL"),
+    (dict(beta=None), E_NULL, "beta is NULL"),
+    (dict(readings=None), E_NULL, "readings is NULL"),
+    (dict(q_idx=None), E_NULL, "q_idx is NULL"),
+    (dict(bank=A + 1), E_ALIGN, "aligned"),
+    (dict(k_idx=A + 1024 * MB + 4), E_ALIGN, "aligned"),
+    (dict(g=A + 1500 * MB + 2), E_ALIGN, "aligned"),
+    (dict(readings=A + 2 * 128 * 100), E_OVERLAP, "overlap"),
+    (dict(readings=A - 2 * 128 * 8 + 2), E_OVERLAP, "overlap"),
+    (dict(num_slots=1 << 62, head_dim=1 << 10), E_SHAPE, "overflow"),
+    (dict(streams=1 << 31), E_SHAPE, "2^31-1 streams"),
+])
+def test_decode_rejects(kw, code, text):
+    rc, msg = call_decode(**kw)
+    assert rc == code, msg
+    assert text in msg
+
+
+def test_decode_zero_streams_is_a_no_op():
+    rc, msg = call_decode(streams=0, bank=None, readings=None)
+    assert rc == OK and msg == ""
+
+
+def test_readings_touching_the_last_bank_element_overlap():
+    # bank [1024, 128] bf16 ends at A + 1024 * 128 * 2; readings starting one element
+    # before that end share a byte range with it.
+    rc, msg = call_decode(readings=A + 1024 * 128 * 2 - 2)
+    assert rc == E_OVERLAP
+
+
+# ------------------------------------------------------------------ gather
+def gather_args(**kw):
+    a = dict(bank=A, bank_dtype=BF16, num_slots=1000, head_dim=128, tokens=64, chunk=16, valid=16,
+             chunk_valid=None, idx_dtype=I32, w_dtype=BF16, idx0=A + 1024 * MB, w0=A + 1100 * MB,
+             width0=8, out0=A + 1200 * MB, stash=A + 1300 * MB, idx1=A + 1400 * MB,
+             w1=A + 1500 * MB, width1=5, out1=A + 1600 * MB, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_gather(**kw):
+    a = gather_args(**kw)
+    lib = sdm.library()
+    rc = lib.sdm_gather(a["bank"], a["bank_dtype"], a["num_slots"], a["head_dim"], a["tokens"], a["chunk"],
+                        a["valid"], a["chunk_valid"], a["idx_dtype"], a["w_dtype"], a["idx0"], a["w0"],
+                        a["width0"], a["out0"], a["stash"], a["idx1"], a["w1"], a["width1"], a["out1"],
+                        a["stream"])
+    return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(bank_dtype=I64), E_DTYPE, "bank must be"),
+    (dict(idx_dtype=F32), E_DTYPE, "indices must be"),
+    (dict(w_dtype=I32), E_DTYPE, "weights must be"),
+    (dict(num_slots=0), E_SHAPE, "at least one slot"),
+    (dict(head_dim=0), E_SHAPE, "at least one slot"),
+    (dict(tokens=-16), E_SHAPE, "tokens = k * chunk"),
+    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
+    (dict(chunk=0), E_SHAPE, "tokens = k * chunk"),
+    (dict(valid=17), E_SHAPE, "valid <= chunk"),
+    (dict(valid=-1), E_SHAPE, "valid <= chunk"),
+    (dict(width0=0), E_RANGE, "width0"),
+    (dict(width0=257), E_RANGE, "width0"),
+    (dict(width1=0), E_RANGE, "width1"),
+    (dict(width1=257), E_RANGE, "width1"),
+    (dict(idx1=None), E_NULL, "go together"),
+    (dict(out1=None), E_NULL, "go together"),
+    (dict(idx1=None, w1=None, out1=None, width1=3), E_NULL, "go together"),
+    (dict(bank=None), E_NULL, "required"),
+    (dict(out0=None), E_NULL, "required"),
+    (dict(bank=A + 2, bank_dtype=F32), E_ALIGN, "aligned"),
+    (dict(out0=A + 1200 * MB + 2), E_ALIGN, "aligned"),
+    (dict(chunk_valid=A + 1700 * MB + 1), E_ALIGN, "aligned"),
+    (dict(out0=A + 1000 * 128), E_OVERLAP, "overlap the bank"),
+    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "overlap the bank"),
+    (dict(out1=A + 128), E_OVERLAP, "overlap the bank"),
+    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+])
+def test_gather_rejects(kw, code, text):
+    rc, msg = call_gather(**kw)
+    assert rc == code, msg
+    assert text in msg
+
+
+def test_gather_zero_tokens_is_a_no_op():
+    rc, msg = call_gather(tokens=0, bank=None, out0=None)
+    assert rc == OK and msg == ""
+
+
+def test_last_error_is_per_thread():
+    rc, msg = call_decode(W=0)
+    assert rc == E_RANGE and msg
+    seen = {}
+
+    def other():
+        seen["msg"] = sdm.library().sdm_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert sdm.library().sdm_last_error().decode() == msg
+
+
+def test_python_binding_raises_on_cpu_tensors():
+    import torch
+    bank = torch.zeros(16, 4)
+    idx = torch.zeros(2, 1, dtype=torch.int64)
+    val = torch.zeros(2, 1)
+    with pytest.raises(ValueError, match="is on cpu"):
+        sdm.sdm_decode_step(bank, idx, val, torch.zeros(2, 4), torch.zeros(2, 1), torch.zeros(2, 1),
+                            idx, val)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from sparse_delta_rule_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setenv("SDM_LIBRARY", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.library()

@@ -1,0 +1,158 @@
+"""Parity of the HIP token gather (sdm_gather through the C ABI) with the oracle.
+
+The kernel sums each output in plain ascending order (include/sdm.h), the
+oracle's groups = 1 order, so outputs are compared bit for bit, and so are the
+stash rows (raw copies) and the padding zeros.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from sparse_delta_rule_amd import SdmError, sdm_gather
+from tests.helpers import bits_equal, to_np_bank
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _np(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy()
+    return t.numpy()
+
+
+def run_case(wl: gen.GatherWorkload, seed: int, *, per_chunk: bool, valid=None, stash=True):
+    bank = gen.gather_bank(wl, seed).to(DEV)
+    inp = {k: v.to(DEV) for k, v in gen.gather_inputs(wl, seed).items()}
+    two = wl.width1 > 0
+    cv = inp["chunk_valid"] if per_chunk else None
+    out0, st, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, valid=valid, chunk_valid=cv,
+                                idx1=inp.get("idx1"), w1=inp.get("w1"), with_stash=stash)
+    torch.cuda.synchronize()
+    ref0, ref_st, ref1 = oracle.gather(
+        to_np_bank(bank), _np(inp["idx0"]), _np(inp["w0"]), chunk=wl.chunk, valid=valid,
+        chunk_valid=None if cv is None else _np(cv), idx1=_np(inp["idx1"]) if two else None,
+        w1=_np(inp["w1"]) if two else None, stash=stash)
+    assert bits_equal(_np(out0), ref0), "operand 0 outputs differ"
+    if two:
+        assert bits_equal(_np(out1), ref1), "operand 1 outputs differ"
+    if stash:
+        assert bits_equal(to_np_bank(st), ref_st), "stash differs"
+    else:
+        assert st is None
+
+
+CASES = [
+    # name, bank dtype, slots, hd, tokens, chunk, width0, width1, idx dtype, w dtype
+    ("hd128 bf16 two ops (c3 shape, small)", torch.bfloat16, 5000, 128, 256, 64, 64, 64, torch.int32, torch.bfloat16),
+    ("hd1 f32 one op", torch.float32, 100, 1, 48, 8, 3, 0, torch.int64, torch.float32),
+    ("hd3 bf16 element vectors", torch.bfloat16, 300, 3, 40, 5, 7, 2, torch.int32, torch.float32),
+    ("hd8 f32 w=1", torch.float32, 64, 8, 32, 32, 1, 1, torch.int64, torch.bfloat16),
+    ("hd64 f32 widths 256/5", torch.float32, 2000, 64, 24, 4, 256, 5, torch.int32, torch.float32),
+    ("hd100 bf16 200-B rows", torch.bfloat16, 3000, 100, 60, 6, 17, 33, torch.int64, torch.bfloat16),
+    ("hd100 f32 400-B rows", torch.float32, 3000, 100, 64, 16, 31, 0, torch.int32, torch.float32),
+    ("hd127 bf16 odd", torch.bfloat16, 1000, 127, 30, 10, 12, 9, torch.int32, torch.bfloat16),
+    ("hd129 f32 odd", torch.float32, 1000, 129, 30, 3, 10, 0, torch.int64, torch.float32),
+    ("hd256 bf16 32 lanes", torch.bfloat16, 1000, 256, 40, 20, 20, 256, torch.int32, torch.bfloat16),
+    ("hd600 bf16 two slices", torch.bfloat16, 500, 600, 16, 8, 9, 4, torch.int32, torch.float32),
+    ("hd1000 f32 four slices", torch.float32, 200, 1000, 8, 4, 5, 3, torch.int64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("padding", ["per_chunk", "scalar", "none", "all"])
+def test_small_cases(case, padding):
+    name, dt, slots, hd, T, chunk, W0, W1, idt, wdt = case
+    wl = gen.GatherWorkload(name=name, bank_dtype=dt, num_slots=slots, head_dim=hd, tokens=T, chunk=chunk,
+                            valid_low=0, valid_high=chunk, width0=W0, width1=W1, idx_dtype=idt, w_dtype=wdt,
+                            bank_std=0.5)
+    valid = {"per_chunk": None, "scalar": max(1, chunk // 2), "none": chunk, "all": 0}[padding]
+    run_case(wl, 11, per_chunk=padding == "per_chunk", valid=valid)
+
+
+@pytest.mark.parametrize("stash", [True, False])
+def test_without_stash(stash):
+    wl = gen.WORKLOADS["c3"].replace(num_slots=20000, tokens=512)
+    run_case(wl, 12, per_chunk=True, stash=stash)
+
+
+def test_misaligned_views_take_narrow_vectors():
+    """Outputs and bank views offset by one element: still exact (narrower vectors)."""
+    wl = gen.WORKLOADS["c3"].replace(num_slots=4000, tokens=64, chunk=16)
+    bank_full = gen.gather_bank(wl.replace(num_slots=4001), 13).to(DEV)
+    bank = bank_full.view(-1)[1:1 + 4000 * 128].view(4000, 128)  # 2 bytes past 16-B alignment
+    inp = {k: v.to(DEV) for k, v in gen.gather_inputs(wl, 13).items()}
+    out_buf = torch.empty(64 * 128 + 1, device=DEV)
+    out0 = out_buf[1:].view(64, 128)
+    o0, st, o1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=16, chunk_valid=inp["chunk_valid"][:4],
+                            idx1=inp["idx1"], w1=inp["w1"], out0=out0)
+    ref0, ref_st, ref1 = oracle.gather(to_np_bank(bank.contiguous()), _np(inp["idx0"]), _np(inp["w0"]), chunk=16,
+                                       chunk_valid=_np(inp["chunk_valid"][:4]), idx1=_np(inp["idx1"]),
+                                       w1=_np(inp["w1"]))
+    assert bits_equal(_np(o0), ref0) and bits_equal(_np(o1), ref1) and bits_equal(to_np_bank(st), ref_st)
+
+
+def test_errors_from_python():
+    bank = torch.zeros(10, 4, device=DEV)
+    idx = torch.zeros(6, 2, dtype=torch.int32, device=DEV)
+    w = torch.zeros(6, 2, device=DEV)
+    with pytest.raises(SdmError, match="SDM_E_SHAPE"):
+        sdm_gather(bank, idx, w, chunk=4)
+    with pytest.raises(SdmError, match="SDM_E_OVERLAP"):
+        sdm_gather(bank, idx, w, chunk=3, out0=bank.view(-1)[:24].view(6, 4), with_stash=False)
+    e = torch.zeros(0, 2, dtype=torch.int32, device=DEV)
+    o, s, _ = sdm_gather(bank, e, torch.zeros(0, 2, device=DEV), chunk=4)
+    assert o.shape == (0, 4) and s.shape == (0, 2, 4)
+
+
+@pytest.mark.slow
+def test_full_size_c3():
+    """Config c3 at full size: sampled tokens against the oracle bit for bit; every
+    padding token zero and every live stash row equal to its bank row."""
+    wl = gen.WORKLOADS["c3"]
+    _say("c3:", wl.name)
+    bank = gen.gather_bank(wl, 0, DEV)
+    inp = gen.gather_inputs(wl, 0, DEV)
+    out0, stash, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+                                   idx1=inp["idx1"], w1=inp["w1"])
+    torch.cuda.synchronize()
+    T = wl.tokens
+    t = torch.arange(T, device=DEV)
+    live = (t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]
+    _say(f"  live tokens {int(live.sum())} of {T}")
+    # padding: zero bits everywhere
+    assert not out0[~live].view(torch.int32).any() and not out1[~live].view(torch.int32).any()
+    assert not stash[~live].view(torch.int16).any()
+    # stash: raw rows of operand 0 for every live token (checked in slices)
+    lt = t[live]
+    for i in range(0, lt.numel(), 2048):
+        sel = lt[i:i + 2048]
+        rows = bank[inp["idx0"][sel].long()]
+        assert torch.equal(stash[sel].view(torch.int16), rows.view(torch.int16))
+    # sampled tokens against the oracle (bank rows they touch, renumbered)
+    g = torch.Generator().manual_seed(1)
+    sample = torch.cat([torch.randperm(T, generator=g)[:1024], torch.arange(0, 128)]).unique().to(DEV)
+    idx0 = inp["idx0"][sample].long()
+    idx1 = inp["idx1"][sample].long()
+    uniq, inv = torch.unique(torch.cat([idx0.ravel(), idx1.ravel()]), return_inverse=True)
+    sub_bank = to_np_bank(bank[uniq])
+    n0 = idx0.numel()
+    i0 = inv[:n0].view_as(idx0).cpu().numpy()
+    i1 = inv[n0:].view_as(idx1).cpu().numpy()
+    live_s = live[sample].cpu().numpy().astype(np.int32)
+    # one-token chunks whose valid count is the token's liveness reproduce the padding rule
+    ref0, ref_st, ref1 = oracle.gather(sub_bank, i0, _np(inp["w0"][sample]), chunk=1, chunk_valid=live_s,
+                                       idx1=i1, w1=_np(inp["w1"][sample]))
+    assert bits_equal(_np(out0[sample]), ref0)
+    assert bits_equal(_np(out1[sample]), ref1)
+    assert bits_equal(to_np_bank(stash[sample]), ref_st)
+    del bank, stash
+    torch.cuda.empty_cache()
