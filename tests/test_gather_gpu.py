@@ -86,7 +86,7 @@ def test_without_stash(stash):
 
 def test_misaligned_views_take_narrow_vectors():
     """Outputs and bank views offset by one element: still exact (narrower vectors)."""
-    wl = gen.WORKLOADS["c3"].replace(num_slots=4000, tokens=64, chunk=16)
+    wl = gen.WORKLOADS["c3"].replace(num_slots=4000, tokens=64, chunk=16, valid_low=4, valid_high=16)
     bank_full = gen.gather_bank(wl.replace(num_slots=4001), 13).to(DEV)
     bank = bank_full.view(-1)[1:1 + 4000 * 128].view(4000, 128)  # 2 bytes past 16-B alignment
     inp = {k: v.to(DEV) for k, v in gen.gather_inputs(wl, 13).items()}
