@@ -69,7 +69,7 @@ enum {
  * nearest to exp(g) (computed in double).
  *
  * Summation order (fixed, a function of W and R only): with
- *     RG = min(32, next_pow2(ceil(max(W, R) / 8)))
+ *     RG = min(32, next_pow2(ceil(max(W, R) / 4)))
  * each column's retrieved is ((0 + p_0) + p_1) + ... + p_{RG-1}, where p_j is
  * the fused multiply-add chain over w = j, j + RG, j + 2 RG, ... ascending,
  * starting from +0, of (k_val[w] d[w]) * row_w (the product k_val[w] d[w]

@@ -9,11 +9,15 @@
 // so each row is read with 16-byte loads (narrower when a row is not a multiple
 // of 16 bytes) and each lane accumulates its own columns. A lane walks the
 // entries in ascending order, one fused multiply-add chain per output element:
-// no cross-lane reduction, no LDS and no barrier, and the result depends on the
-// inputs alone. Entries are taken NB at a time per operand, with all of a
-// batch's row loads issued before the first is used, so NB (one operand) or
-// 2 * NB (two operands) random rows per lane are in flight; the HBM latency is
-// hidden by that and by the many tokens resident per CU.
+// no cross-lane reduction, and the result depends on the inputs alone.
+//
+// Memory pipeline: the slots and weights of the block's live tokens are staged
+// in LDS with contiguous loads (CH entries per token at a time), so the only
+// global round trips inside a token's loop are its row loads. Entries are then
+// taken NB at a time (both operands together while both have entries), all of
+// a batch's row loads issued before the first is used; the HBM latency is
+// hidden by those and by the many tokens resident per CU. Padding tokens read
+// no slot, weight or row.
 
 #include "sdm_kernels.h"
 
@@ -22,22 +26,88 @@ namespace sdm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kStageEntries = 1024;  // tokens per block x entries per token staged at once
 
-template <typename E, int VB, bool TWO, int NB>
+// N consecutive entries [n0, n0 + N) of the operands selected by DO0 / DO1, all
+// valid: every row load is issued before the first row is used, and nothing
+// in between is conditional (a guarded use would let the compiler move its
+// load next to it and wait there).
+template <typename E, int VB, int N, bool DO0, bool DO1, typename IdxT, typename WT>
+__device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t hd, int64_t col, int n0, int krel,
+                                             const IdxT* s_idx0, const WT* s_w0, const IdxT* s_idx1,
+                                             const WT* s_w1, E* stash_row, float (&acc0)[VB / sizeof(E)],
+                                             float (&acc1)[VB / sizeof(E)]) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+    V r0[N], r1[N];
+    float x0[N], x1[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (DO0) {
+            r0[i] = *reinterpret_cast<const V*>(bank + int64_t(s_idx0[krel + i]) * hd + col);
+            x0[i] = value_of<WT>(s_w0[krel + i]);
+        }
+        if (DO1) {
+            r1[i] = *reinterpret_cast<const V*>(bank + int64_t(s_idx1[krel + i]) * hd + col);
+            x1[i] = value_of<WT>(s_w1[krel + i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (DO0) {
+            if (stash_row != nullptr) *reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col) = r0[i];
+            E el[VEC];
+            __builtin_memcpy(el, &r0[i], VB);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc0[e] = __builtin_fmaf(x0[i], widen(el[e]), acc0[e]);
+        }
+        if (DO1) {
+            E el[VEC];
+            __builtin_memcpy(el, &r1[i], VB);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc1[e] = __builtin_fmaf(x1[i], widen(el[e]), acc1[e]);
+        }
+    }
+}
+
+template <typename E, int VB, bool TWO, int NB, typename IdxT, typename WT>
 __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams p) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
+    extern __shared__ __align__(16) char s_raw[];
+
     const int tid = threadIdx.x;
+    const int tpb = kThreads / p.lpr;      // tokens per block
+    const int ch = kStageEntries / tpb;    // entries per token staged at once
     const int lane = tid & (p.lpr - 1);
-    const int64_t t = int64_t(blockIdx.x) * (kThreads / p.lpr) + tid / p.lpr;
+    const int g = tid / p.lpr;
+    const int64_t t_first = int64_t(blockIdx.x) * tpb;
+    const int64_t t = t_first + g;
     const int vi = int(blockIdx.y) * p.lpr + lane;
-    if (t >= p.tokens || vi >= p.vpr) return;
-    const int64_t col = int64_t(vi) * VEC;
-    const int64_t chunk_no = t / p.chunk;
-    const int64_t limit = p.chunk_valid != nullptr ? int64_t(p.chunk_valid[chunk_no]) : p.valid;
-    const bool live = (t - chunk_no * p.chunk) < limit;
+    const bool lane_on = t < p.tokens && vi < p.vpr;
+    const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
+
+    // LDS: [tpb][ch] slots and weights per operand, then one live flag per token.
+    IdxT* s_idx0 = reinterpret_cast<IdxT*>(s_raw);
+    IdxT* s_idx1 = s_idx0 + tpb * ch;
+    WT* s_w0 = reinterpret_cast<WT*>(s_idx1 + (TWO ? tpb * ch : 0));
+    WT* s_w1 = s_w0 + tpb * ch;
+    int* s_live = reinterpret_cast<int*>(s_w1 + (TWO ? tpb * ch : 0));
+
+    bool live = false;
+    if (t < p.tokens) {
+        const int64_t chunk_no = t / p.chunk;
+        const int64_t limit = p.chunk_valid != nullptr ? int64_t(p.chunk_valid[chunk_no]) : p.valid;
+        live = (t - chunk_no * p.chunk) < limit;
+    }
+    if (lane == 0) s_live[g] = live ? 1 : 0;
+
     const E* bank = static_cast<const E*>(p.bank);
-    E* stash = static_cast<E*>(p.stash);
+    E* stash_row = p.stash != nullptr && lane_on ? static_cast<E*>(p.stash) + t * p.width0 * p.hd : nullptr;
+    const IdxT* idx0 = static_cast<const IdxT*>(p.idx0);
+    const IdxT* idx1 = static_cast<const IdxT*>(p.idx1);
+    const WT* w0 = static_cast<const WT*>(p.w0);
+    const WT* w1 = static_cast<const WT*>(p.w1);
 
     float acc0[VEC], acc1[VEC];
 #pragma unroll
@@ -46,52 +116,60 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         acc1[e] = 0.0f;
     }
 
-    if (!live) {
-        if (stash != nullptr) {
-            V zero;
-            __builtin_memset(&zero, 0, VB);
-            for (int n = 0; n < p.width0; ++n)
-                *reinterpret_cast<V*>(stash + (t * p.width0 + n) * p.hd + col) = zero;
-        }
-    } else {
-        const int wmax = TWO && p.width1 > p.width0 ? p.width1 : p.width0;
-        for (int n0 = 0; n0 < wmax; n0 += NB) {
-            // Every load is unconditional: an entry past an operand's width re-reads
-            // that operand's last entry and is ignored. Guarded loads would let the
-            // compiler wait for each row next to its load.
-            V r0[NB], r1[NB];
-            float w0[NB], w1[NB];
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int n = n0 + i;
-                const int64_t at = t * p.width0 + (n < p.width0 ? n : p.width0 - 1);
-                r0[i] = *reinterpret_cast<const V*>(bank + load_slot(p.idx0, at, p.idx64) * p.hd + col);
-                w0[i] = load_value(p.w0, at, p.w_bf16);
-                if (TWO) {
-                    const int64_t at1 = t * p.width1 + (n < p.width1 ? n : p.width1 - 1);
-                    r1[i] = *reinterpret_cast<const V*>(bank + load_slot(p.idx1, at1, p.idx64) * p.hd + col);
-                    w1[i] = load_value(p.w1, at1, p.w_bf16);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int n = n0 + i;
+    if (!live && stash_row != nullptr) {
+        V zero;
+        __builtin_memset(&zero, 0, VB);
+        for (int n = 0; n < p.width0; ++n) *reinterpret_cast<V*>(stash_row + int64_t(n) * p.hd + col) = zero;
+    }
+
+    const int wmax = TWO && p.width1 > p.width0 ? p.width1 : p.width0;
+    for (int base = 0; base < wmax; base += ch) {
+        // ---- stage entries [base, base + ch) of every live token of the block.
+        __syncthreads();  // s_live written; the previous chunk's entries consumed
+        for (int k = tid; k < tpb * ch; k += kThreads) {
+            const int tt = k / ch, n = base + (k - tt * ch);
+            const int64_t tok = t_first + tt;
+            if (tok < p.tokens && s_live[tt]) {
                 if (n < p.width0) {
-                    if (stash != nullptr) *reinterpret_cast<V*>(stash + (t * p.width0 + n) * p.hd + col) = r0[i];
-                    E el[VEC];
-                    __builtin_memcpy(el, &r0[i], VB);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc0[e] = __builtin_fmaf(w0[i], widen(el[e]), acc0[e]);
+                    s_idx0[k] = idx0[tok * p.width0 + n];
+                    s_w0[k] = w0[tok * p.width0 + n];
                 }
                 if (TWO && n < p.width1) {
-                    E el[VEC];
-                    __builtin_memcpy(el, &r1[i], VB);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc1[e] = __builtin_fmaf(w1[i], widen(el[e]), acc1[e]);
+                    s_idx1[k] = idx1[tok * p.width1 + n];
+                    s_w1[k] = w1[tok * p.width1 + n];
                 }
             }
         }
+        __syncthreads();
+        if (!(live && lane_on)) continue;
+
+        // ---- entries in ascending order: full batches of both operands, then of
+        // each operand alone, then single entries.
+        const int k_base = g * ch - base;  // LDS index of entry n is k_base + n
+        const int end0 = min(p.width0, base + ch);
+        const int end1 = TWO ? min(p.width1, base + ch) : base;
+        int n = base;
+        if (TWO)
+            for (; n + NB <= min(end0, end1); n += NB)
+                gather_batch<E, VB, NB, true, true>(bank, p.hd, col, n, k_base + n, s_idx0, s_w0, s_idx1, s_w1,
+                                                    stash_row, acc0, acc1);
+        int n_0 = n, n_1 = n;
+        for (; n_0 + NB <= end0; n_0 += NB)
+            gather_batch<E, VB, NB, true, false>(bank, p.hd, col, n_0, k_base + n_0, s_idx0, s_w0, s_idx1, s_w1,
+                                                 stash_row, acc0, acc1);
+        for (; n_0 < end0; ++n_0)
+            gather_batch<E, VB, 1, true, false>(bank, p.hd, col, n_0, k_base + n_0, s_idx0, s_w0, s_idx1, s_w1,
+                                                stash_row, acc0, acc1);
+        if (TWO) {
+            for (; n_1 + NB <= end1; n_1 += NB)
+                gather_batch<E, VB, NB, false, true>(bank, p.hd, col, n_1, k_base + n_1, s_idx0, s_w0, s_idx1,
+                                                     s_w1, stash_row, acc0, acc1);
+            for (; n_1 < end1; ++n_1)
+                gather_batch<E, VB, 1, false, true>(bank, p.hd, col, n_1, k_base + n_1, s_idx0, s_w0, s_idx1,
+                                                    s_w1, stash_row, acc0, acc1);
+        }
     }
+    if (!lane_on) return;
 
     float* o0 = p.out0 + t * p.hd + col;
     float* o1 = TWO ? p.out1 + t * p.hd + col : nullptr;
@@ -110,16 +188,29 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     }
 }
 
-template <typename E, int VB>
-hipError_t launch_vb(const GatherParams& p, const GatherGeometry& geo, bool two, hipStream_t stream) {
+template <typename E, int VB, bool TWO, typename IdxT, typename WT>
+hipError_t launch_typed(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
     const int64_t blocks = (p.tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
     const dim3 grid(unsigned(blocks), unsigned(geo.slices));
     const dim3 block(kThreads);
-    if (two)
-        hipLaunchKernelGGL((sdm_gather_kernel<E, VB, true, 4>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((sdm_gather_kernel<E, VB, false, 8>), grid, block, 0, stream, p);
+    const size_t lds = size_t(kStageEntries) * (TWO ? 2 : 1) * (sizeof(IdxT) + sizeof(WT)) +
+                       size_t(geo.tokens_per_block) * sizeof(int);
+    hipLaunchKernelGGL((sdm_gather_kernel<E, VB, TWO, TWO ? 4 : 8, IdxT, WT>), grid, block, lds, stream, p);
     return hipGetLastError();
+}
+
+template <typename E, int VB, bool TWO>
+hipError_t launch_ops(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
+    if (p.idx64)
+        return p.w_bf16 ? launch_typed<E, VB, TWO, int64_t, uint16_t>(p, geo, stream)
+                        : launch_typed<E, VB, TWO, int64_t, float>(p, geo, stream);
+    return p.w_bf16 ? launch_typed<E, VB, TWO, int32_t, uint16_t>(p, geo, stream)
+                    : launch_typed<E, VB, TWO, int32_t, float>(p, geo, stream);
+}
+
+template <typename E, int VB>
+hipError_t launch_vb(const GatherParams& p, const GatherGeometry& geo, bool two, hipStream_t stream) {
+    return two ? launch_ops<E, VB, true>(p, geo, stream) : launch_ops<E, VB, false>(p, geo, stream);
 }
 
 int pow2_ceil(int64_t x) {

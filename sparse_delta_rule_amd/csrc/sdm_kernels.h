@@ -31,6 +31,19 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
     return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);
 }
 
+// Make a register's contents opaque to the optimiser (no instruction is
+// emitted): values derived from it before this point are not reused after it.
+__device__ __forceinline__ void opaque(uint4& v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void opaque(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint16_t& v) {
+    uint32_t w = v;
+    asm volatile("" : "+v"(w));
+    v = uint16_t(w);
+}
+
 template <typename E> __device__ __forceinline__ E narrow(float f);
 template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float f) { return to_bf16_rne(f); }
 template <> __device__ __forceinline__ float narrow<float>(float f) { return f; }
@@ -38,14 +51,10 @@ template <> __device__ __forceinline__ float narrow<float>(float f) { return f; 
 // Round a float32 to the bank element type and widen it back.
 template <typename E> __device__ __forceinline__ float to_bank(float f) { return widen(narrow<E>(f)); }
 
-// A value or weight given as float32 or bfloat16.
-__device__ __forceinline__ float load_value(const void* p, int64_t i, bool bf16) {
-    return bf16 ? widen(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
-}
-
-__device__ __forceinline__ int64_t load_slot(const void* p, int64_t i, bool i64) {
-    return i64 ? static_cast<const int64_t*>(p)[i] : int64_t(static_cast<const int32_t*>(p)[i]);
-}
+// A value or weight given as float32 or bfloat16 (raw bits), as float32.
+template <typename T> __device__ __forceinline__ float value_of(T x);
+template <> __device__ __forceinline__ float value_of<float>(float x) { return x; }
+template <> __device__ __forceinline__ float value_of<uint16_t>(uint16_t x) { return widen(x); }
 
 // ------------------------------------------------------------------ decode
 struct DecodeParams {

@@ -97,8 +97,8 @@ def random_decode_case(rng: np.random.Generator, *, streams, slots_per_stream, h
 # ----------------------------------------------------------------- GPU runs
 def documented_decode_groups(W: int, R: int) -> int:
     """The decode's row-group count as include/sdm.h states it:
-    RG = min(32, next_pow2(ceil(max(W, R) / 8)))."""
-    need = -(-max(W, R) // 8)
+    RG = min(32, next_pow2(ceil(max(W, R) / 4)))."""
+    need = -(-max(W, R) // 4)
     rg = 1
     while rg < need:
         rg *= 2
