@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Throughput of the sparse-delta-memory hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--seed S]
+    python bench.py [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--entry steps|step]
 
-A step is one sdm_decode_step over every stream of the workload (one token
-per stream), or one sdm_gather launch over every token (--config c3). Inputs
+A step is one decode token for every stream of the workload (one pass of the
+decode step), or one sdm_gather launch over every token (--config c3). Inputs
 are seeded and synthetic (gen/), generated on the GPU and resident in HBM
-before the timed region; the decode cycles through the workload's token
-sequence, the bank changing from step to step as the method intends. The
-timed steps run as one HIP-graph replay (``--launch eager`` launches from
-Python instead) bracketed by HIP events on the stream the kernels run on.
+before the timed region; the decode runs the workload's token sequence, the
+bank changing from token to token as the method intends. By default a decode
+launch is one sdm_decode_steps call over the whole sequence (K must be a
+multiple of its length); ``--entry step`` launches sdm_decode_step once per
+token instead. The timed launches run as one HIP-graph replay (``--launch
+eager`` launches from Python instead) bracketed by HIP events on the stream
+the kernels run on.
 
 Prints one JSON line: stream-steps/s (tokens/s for the gather), the achieved
 bank-row bandwidth against the MI355X's 8 TB/s HBM peak, and the CPU oracle
@@ -42,15 +45,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(config: str):
-    """HBM bytes per launch measured by rocprofv3 counters for this config, if they were
-    taken on the current kernel sources (profiles/traffic.json), else None."""
+def stored_traffic(config: str, kernel: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this config and kernel,
+    if they were taken on the current kernel sources (profiles/traffic.json), else None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    entry = data.get(config)
+    entry = data.get(f"{config}/{kernel}")
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
     return entry.get("bytes_per_launch")
@@ -64,6 +67,9 @@ def parse_args(argv=None):
     p.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    p.add_argument("--entry", default="steps", choices=["steps", "step"],
+                   help="decode: one sdm_decode_steps launch per token sequence (steps), or one "
+                        "sdm_decode_step launch per token (step)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -172,34 +178,52 @@ def cpu_baseline_gather(torch, wl, bank, inp, live, target_s, cfg_name):
 # ------------------------------------------------------------------ workloads
 def bench_decode(torch, args, cfg_name, wl):
     import gen
-    from sparse_delta_rule_amd import sdm_decode_step
+    from sparse_delta_rule_amd import sdm_decode_step, sdm_decode_steps
     dev = torch.device("cuda", 0)
     es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    T = wl.steps
     bank = gen.decode_bank(wl, args.seed, dev)
-    seq = [gen.decode_step_inputs(wl, args.seed, t, dev) for t in range(wl.steps)]
-    readings = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
+    seq = [gen.decode_step_inputs(wl, args.seed, t, dev) for t in range(T)]
     torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_decode(torch, wl, bank, seq, args.cpu_seconds, cfg_name)
-    K = args.steps if args.steps is not None else wl.steps
+    K = args.steps if args.steps is not None else T
+    row_bytes_step = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
+    if args.entry == "steps":
+        if K % T:
+            raise SystemExit(f"bench.py: --steps must be a multiple of the {T}-token sequence with --entry steps")
+        stacked = {k: torch.stack([d[k] for d in seq]) for k in seq[0]}
+        del seq
+        readings = torch.empty((T, wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev)
 
-    def launch_one(i):
-        j = i % len(seq)
-        sdm_decode_step(bank, **seq[j], readings=readings[j])
+        def launch_one(i):
+            sdm_decode_steps(bank, **stacked, readings=readings)
 
-    ms = _run_steps(torch, args, launch_one, K)
+        launches, per_launch = K // T, T
+        kernel = "sdm_decode_steps_kernel"
+    else:
+        readings = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
+
+        def launch_one(i):
+            j = i % len(seq)
+            sdm_decode_step(bank, **seq[j], readings=readings[j])
+
+        launches, per_launch = K, 1
+        kernel = "sdm_decode_kernel"
+    ms = _run_steps(torch, args, launch_one, launches)
     ms_step = ms / K
-    row_bytes = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
-    gbps = row_bytes / (ms_step * 1e-3) / 1e9
+    launch_bytes = row_bytes_step * per_launch
+    gbps = launch_bytes / (ms / launches * 1e-3) / 1e9
     config = {"workload": f"{cfg_name}: {wl.name}", "streams": wl.streams, "slots": wl.num_slots,
               "head_dim": wl.head_dim, "W": wl.W, "R": wl.R, "G": wl.G,
               "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "index_dtype":
-              str(wl.idx_dtype).replace("torch.", ""), "sequence_steps": wl.steps, "launch": args.launch,
-              "seed": args.seed}
+              str(wl.idx_dtype).replace("torch.", ""), "sequence_steps": T,
+              "entry": "sdm_decode_steps" if args.entry == "steps" else "sdm_decode_step",
+              "tokens_per_launch": per_launch, "launch": args.launch, "seed": args.seed}
     value = wl.streams * K / (ms * 1e-3)
     return dict(value=value, unit="stream-steps/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=row_bytes, kernel="sdm_decode_kernel", cpu=cpu, tokens_per_s=value)
+                row_bytes=launch_bytes, kernel=kernel, cpu=cpu, tokens_per_s=value)
 
 
 def bench_gather(torch, args, cfg_name, wl):
@@ -273,7 +297,7 @@ def main(argv=None):
         r = bench_decode(torch, args, args.config, wl)
     else:
         r = bench_gather(torch, args, args.config, wl)
-    traffic = stored_traffic(args.config)
+    traffic = stored_traffic(args.config, r["kernel"])
     out = {
         "metric": METRIC,
         "value": r["value"],

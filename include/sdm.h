@@ -110,6 +110,33 @@ int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_
                     void* readings, void* hip_stream);
 
 /*
+ * sdm_decode_steps: advance every stream by `steps` tokens in one call.
+ *
+ * Operation: exactly `steps` successive sdm_decode_step calls (same results,
+ * bit for bit), token t of every stream before token t + 1; the pages' decode
+ * step is the single-token case of this multi-token recurrence (page
+ * "sparse_delta_memory/decode.py", docstring of sdm_decode_step). One launch
+ * keeps each stream's workgroup resident across its tokens and overlaps a
+ * token's reads with the next token's row loads, for workloads where a single
+ * step is too small to cover launch and memory latency.
+ *
+ * Arguments: as sdm_decode_step, each per-token array gaining a leading
+ * [steps] axis (token-major, contiguous): k_idx, k_val [steps, streams, W];
+ * v [steps, streams, head_dim]; beta [steps, streams]; g [steps, streams, G];
+ * q_idx, q_val [steps, streams, R]; readings [steps, streams, head_dim] (must not
+ * overlap the bank). steps >= 0; steps == 0 or streams == 0 enqueues nothing.
+ * The preconditions apply to every token (slots of one stream stay private to
+ * it across all tokens of the call). Errors: as sdm_decode_step.
+ */
+int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                     int64_t steps, int64_t streams, int32_t W, int32_t R, int32_t G,
+                     const void* k_idx, int k_idx_dtype,
+                     const void* k_val, const void* v, const void* q_val, int val_dtype,
+                     const float* beta, const float* g,
+                     const void* q_idx, int q_idx_dtype,
+                     void* readings, void* hip_stream);
+
+/*
  * sdm_gather: per-token weighted sums of bank rows, with a raw copy of the rows.
  *
  * Operation (page "sparse_delta_memory/cuda/gather_cuda.py", module docstring;

@@ -6,6 +6,7 @@ tensors (device memory and streams) into those calls: it has no fallback, and
 every entry point raises if the library is not built or a call fails.
 
     readings = sdm_decode_step(bank, k_idx, k_val, v, beta, g, q_idx, q_val)
+    readings = sdm_decode_steps(bank, k_idx, k_val, v, beta, g, q_idx, q_val)  # [steps, ...] inputs
     out0, stash, out1 = sdm_gather(bank, idx0, w0, chunk=64, valid=64, idx1=..., w1=...)
 """
 
@@ -20,5 +21,6 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     sdm_decode_step,
+    sdm_decode_steps,
     sdm_gather,
 )

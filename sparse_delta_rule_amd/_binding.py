@@ -54,6 +54,9 @@ def library() -> ctypes.CDLL:
     lib.sdm_decode_step.argtypes = [P, i32, i64, i64, i64, i32, i32, i32, P, i32, P, P, P, i32,
                                     P, P, P, i32, P, P]
     lib.sdm_decode_step.restype = ctypes.c_int
+    lib.sdm_decode_steps.argtypes = [P, i32, i64, i64, i64, i64, i32, i32, i32, P, i32, P, P, P, i32,
+                                     P, P, P, i32, P, P]
+    lib.sdm_decode_steps.restype = ctypes.c_int
     lib.sdm_gather.argtypes = [P, i32, i64, i64, i64, i64, i64, P, i32, i32, P, P, i32, P, P,
                                P, P, i32, P, P]
     lib.sdm_gather.restype = ctypes.c_int
@@ -132,6 +135,48 @@ def sdm_decode_step(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor
     streams = k_idx.numel() // W
     rc = library().sdm_decode_step(
         _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, streams, W, R, G,
+        _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
+        _ptr(beta), _ptr(g), _ptr(q_idx), _dt(q_idx, "q_idx"), _ptr(readings),
+        _stream_handle(bank.device))
+    if rc != 0:
+        _raise(rc)
+    return readings
+
+
+def sdm_decode_steps(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
+                     beta: torch.Tensor, g: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor,
+                     readings: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``steps`` decode steps for every stream in one launch (``sdm_decode_steps``).
+
+    Like ``sdm_decode_step`` with a leading token axis on every per-token input:
+    k_idx, k_val [steps, ..., W]; v [steps, ..., head_dim]; beta [steps, ..., 1];
+    g [steps, ..., G]; q_idx, q_val [steps, ..., R]. Token t of every stream is
+    applied before token t + 1; the result equals ``steps`` single-step calls.
+    Returns readings shaped like ``v`` in the bank dtype.
+    """
+    if bank.dim() != 2 or k_idx.dim() < 2:
+        raise ValueError("bank must be [num_slots, head_dim] and k_idx [steps, ..., W]")
+    hd = bank.shape[1]
+    W, R, G = k_idx.shape[-1], q_idx.shape[-1], g.shape[-1]
+    lead = tuple(k_idx.shape[:-1])
+    for name, t, n in (("k_val", k_val, W), ("v", v, hd), ("beta", beta, 1), ("g", g, G),
+                       ("q_idx", q_idx, R), ("q_val", q_val, R)):
+        if tuple(t.shape) != lead + (n,):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {lead + (n,)}")
+    if not (k_val.dtype == v.dtype == q_val.dtype):
+        raise TypeError("k_val, v and q_val must share one dtype")
+    if beta.dtype != torch.float32 or g.dtype != torch.float32:
+        raise TypeError("beta and g must be float32")
+    if readings is None:
+        readings = torch.empty(v.shape, dtype=bank.dtype, device=bank.device)
+    elif tuple(readings.shape) != tuple(v.shape) or readings.dtype != bank.dtype:
+        raise ValueError("readings must be shaped like v, in the bank dtype")
+    _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
+               q_val=q_val, readings=readings)
+    steps = lead[0]
+    streams = k_idx.numel() // (W * steps) if steps else 0
+    rc = library().sdm_decode_steps(
+        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, steps, streams, W, R, G,
         _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
         _ptr(beta), _ptr(g), _ptr(q_idx), _dt(q_idx, "q_idx"), _ptr(readings),
         _stream_handle(bank.device))

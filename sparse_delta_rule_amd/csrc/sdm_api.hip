@@ -169,44 +169,50 @@ const char* sdm_last_error(void) { return g_last_error.c_str(); }
 
 int sdm_abi_version(void) { return SDM_ABI_VERSION; }
 
-int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t streams,
-                    int32_t W, int32_t R, int32_t G, const void* k_idx, int k_idx_dtype, const void* k_val,
-                    const void* v, const void* q_val, int val_dtype, const float* beta, const float* g,
-                    const void* q_idx, int q_idx_dtype, void* readings, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by sdm_decode_step (steps = 1, per-step arrays) and sdm_decode_steps.
+int decode_call(const char* fn, void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t steps,
+                int64_t streams, int32_t W, int32_t R, int32_t G, const void* k_idx, int k_idx_dtype,
+                const void* k_val, const void* v, const void* q_val, int val_dtype, const float* beta,
+                const float* g, const void* q_idx, int q_idx_dtype, void* readings, void* hip_stream) {
     if (bank_dtype != SDM_F32 && bank_dtype != SDM_BF16)
-        return fail(SDM_E_DTYPE, "sdm_decode_step: bank must be float32 or bfloat16 (dtype %d)", bank_dtype);
+        return fail(SDM_E_DTYPE, "%s: bank must be float32 or bfloat16 (dtype %d)", fn, bank_dtype);
     if (val_dtype != SDM_F32 && val_dtype != SDM_BF16)
-        return fail(SDM_E_DTYPE, "sdm_decode_step: k_val, v, q_val must be float32 or bfloat16 (dtype %d)",
-                    val_dtype);
+        return fail(SDM_E_DTYPE, "%s: k_val, v, q_val must be float32 or bfloat16 (dtype %d)", fn, val_dtype);
     if ((k_idx_dtype != SDM_I32 && k_idx_dtype != SDM_I64) || (q_idx_dtype != SDM_I32 && q_idx_dtype != SDM_I64))
-        return fail(SDM_E_DTYPE, "sdm_decode_step: k_idx and q_idx must be int32 or int64 (dtypes %d, %d)",
-                    k_idx_dtype, q_idx_dtype);
+        return fail(SDM_E_DTYPE, "%s: k_idx and q_idx must be int32 or int64 (dtypes %d, %d)", fn, k_idx_dtype,
+                    q_idx_dtype);
     if (num_slots < 1 || head_dim < 1)
-        return fail(SDM_E_SHAPE, "sdm_decode_step: the bank needs at least one slot and one column, got [%lld, %lld]",
+        return fail(SDM_E_SHAPE, "%s: the bank needs at least one slot and one column, got [%lld, %lld]", fn,
                     (long long)num_slots, (long long)head_dim);
-    if (streams < 0) return fail(SDM_E_SHAPE, "sdm_decode_step: streams = %lld < 0", (long long)streams);
+    if (streams < 0) return fail(SDM_E_SHAPE, "%s: streams = %lld < 0", fn, (long long)streams);
+    if (steps < 0) return fail(SDM_E_SHAPE, "%s: steps = %lld < 0", fn, (long long)steps);
     if (W < 1 || W > SDM_MAX_WIDTH || R < 1 || R > SDM_MAX_WIDTH)
-        return fail(SDM_E_RANGE, "sdm_decode_step: W and R must be in 1..%d, got W=%d, R=%d", SDM_MAX_WIDTH, W, R);
-    if (G != 1 && G != W)
-        return fail(SDM_E_SHAPE, "sdm_decode_step: G must be 1 or W=%d, got %d", W, G);
+        return fail(SDM_E_RANGE, "%s: W and R must be in 1..%d, got W=%d, R=%d", fn, SDM_MAX_WIDTH, W, R);
+    if (G != 1 && G != W) return fail(SDM_E_SHAPE, "%s: G must be 1 or W=%d, got %d", fn, W, G);
     const int es = elem_size(bank_dtype);
-    if (!mul_fits(num_slots, head_dim, es) || !mul_fits(streams, head_dim, es) || !mul_fits(streams, SDM_MAX_WIDTH, 8))
-        return fail(SDM_E_SHAPE, "sdm_decode_step: sizes overflow 64-bit byte counts");
+    if (!mul_fits(num_slots, head_dim, es) || !mul_fits(steps, streams, head_dim * es) ||
+        !mul_fits(steps, streams, SDM_MAX_WIDTH * 8))
+        return fail(SDM_E_SHAPE, "%s: sizes overflow 64-bit byte counts", fn);
     if (streams > 0x7fffffffLL)
-        return fail(SDM_E_SHAPE, "sdm_decode_step: at most 2^31-1 streams per call, got %lld", (long long)streams);
-    if (streams == 0) return ok();
+        return fail(SDM_E_SHAPE, "%s: at most 2^31-1 streams per call, got %lld", fn, (long long)streams);
+    if (steps > 0x7fffffffLL) return fail(SDM_E_SHAPE, "%s: at most 2^31-1 steps per call", fn);
+    if (streams == 0 || steps == 0) return ok();
     const struct { const void* p; const char* name; } req[] = {
         {bank, "bank"}, {k_idx, "k_idx"}, {k_val, "k_val"}, {v, "v"}, {q_val, "q_val"},
         {beta, "beta"}, {g, "g"}, {q_idx, "q_idx"}, {readings, "readings"}};
     for (const auto& r : req)
-        if (r.p == nullptr) return fail(SDM_E_NULL, "sdm_decode_step: %s is NULL", r.name);
+        if (r.p == nullptr) return fail(SDM_E_NULL, "%s: %s is NULL", fn, r.name);
     const int vs = elem_size(val_dtype);
     if (!aligned(bank, es) || !aligned(readings, es) || !aligned(k_idx, elem_size(k_idx_dtype)) ||
         !aligned(q_idx, elem_size(q_idx_dtype)) || !aligned(k_val, vs) || !aligned(v, vs) || !aligned(q_val, vs) ||
         !aligned(beta, 4) || !aligned(g, 4))
-        return fail(SDM_E_ALIGN, "sdm_decode_step: a pointer is not aligned to its element size");
-    if (overlap(readings, streams * head_dim * es, bank, num_slots * head_dim * es))
-        return fail(SDM_E_OVERLAP, "sdm_decode_step: readings overlap the bank");
+        return fail(SDM_E_ALIGN, "%s: a pointer is not aligned to its element size", fn);
+    if (overlap(readings, steps * streams * head_dim * es, bank, num_slots * head_dim * es))
+        return fail(SDM_E_OVERLAP, "%s: readings overlap the bank", fn);
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (debug_validate()) {
@@ -214,15 +220,21 @@ int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_
             int rc = check_device_ptr(r.p, r.name);
             if (rc != SDM_OK) return rc;
         }
-        int rc = validate_decode_slots(num_slots, streams, W, R, k_idx, k_idx_dtype, q_idx, q_idx_dtype, stream);
-        if (rc != SDM_OK) return rc;
+        const int kb = elem_size(k_idx_dtype), qb = elem_size(q_idx_dtype);
+        for (int64_t t = 0; t < steps; ++t) {
+            int rc = validate_decode_slots(num_slots, streams, W, R,
+                                           static_cast<const char*>(k_idx) + t * streams * W * kb, k_idx_dtype,
+                                           static_cast<const char*>(q_idx) + t * streams * R * qb, q_idx_dtype,
+                                           stream);
+            if (rc != SDM_OK) return rc;
+        }
     }
 
     const sdm::DecodeGeometry geo =
-        sdm::decode_geometry(es, head_dim, W, R, reinterpret_cast<uintptr_t>(bank));
+        sdm::decode_geometry(es, head_dim, W, R, reinterpret_cast<uintptr_t>(bank), steps > 1);
     if (geo.slices > 65535)
-        return fail(SDM_E_SHAPE, "sdm_decode_step: head_dim %lld needs %d column slices (max 65535)",
-                    (long long)head_dim, geo.slices);
+        return fail(SDM_E_SHAPE, "%s: head_dim %lld needs %d column slices (max 65535)", fn, (long long)head_dim,
+                    geo.slices);
     sdm::DecodeParams p{};
     p.bank = bank;
     p.k_idx = k_idx;
@@ -234,18 +246,40 @@ int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_
     p.g = g;
     p.readings = readings;
     p.hd = head_dim;
+    p.streams = streams;
+    p.steps = int(steps);
     p.W = W;
     p.R = R;
     p.G = G;
     p.vpr = geo.vpr;
     p.lpr = geo.lpr;
     p.rg = geo.rg;
-    p.k64 = k_idx_dtype == SDM_I64;
-    p.q64 = q_idx_dtype == SDM_I64;
-    p.val_bf16 = val_dtype == SDM_BF16;
-    hipError_t e = sdm::launch_decode(p, geo, streams, bank_dtype == SDM_BF16, stream);
-    if (e != hipSuccess) return fail(SDM_E_HIP, "sdm_decode_step: launch failed: %s", hipGetErrorString(e));
+    p.k_bytes = elem_size(k_idx_dtype);
+    p.q_bytes = elem_size(q_idx_dtype);
+    p.val_bytes = vs;
+    hipError_t e = sdm::launch_decode(p, geo, bank_dtype == SDM_BF16, stream);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t streams,
+                    int32_t W, int32_t R, int32_t G, const void* k_idx, int k_idx_dtype, const void* k_val,
+                    const void* v, const void* q_val, int val_dtype, const float* beta, const float* g,
+                    const void* q_idx, int q_idx_dtype, void* readings, void* hip_stream) {
+    return decode_call("sdm_decode_step", bank, bank_dtype, num_slots, head_dim, 1, streams, W, R, G, k_idx,
+                       k_idx_dtype, k_val, v, q_val, val_dtype, beta, g, q_idx, q_idx_dtype, readings, hip_stream);
+}
+
+int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t steps,
+                     int64_t streams, int32_t W, int32_t R, int32_t G, const void* k_idx, int k_idx_dtype,
+                     const void* k_val, const void* v, const void* q_val, int val_dtype, const float* beta,
+                     const float* g, const void* q_idx, int q_idx_dtype, void* readings, void* hip_stream) {
+    return decode_call("sdm_decode_steps", bank, bank_dtype, num_slots, head_dim, steps, streams, W, R, G, k_idx,
+                       k_idx_dtype, k_val, v, q_val, val_dtype, beta, g, q_idx, q_idx_dtype, readings, hip_stream);
 }
 
 int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t tokens, int64_t chunk,

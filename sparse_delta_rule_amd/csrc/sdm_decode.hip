@@ -1,30 +1,37 @@
-// SDM decode step on gfx950: one workgroup per (stream, column slice).
+// SDM decode on gfx950: one workgroup per (stream, column slice).
 //
-// The step (page "sparse_delta_memory/decode.py", docstring of sdm_decode_step)
-// gathers the W written rows of a stream, forms retrieved and delta_v per
-// column, writes the W rows back decayed and updated, and reads the R rows back
-// as a weighted sum after the write. Every quantity is per column, so column
-// slices are independent and a workgroup owns all W and R rows of its stream
-// within its slice: only its own stores can change what its reads see (the
-// same argument as the prior-art Triton kernel on that page, whose programs own
-// 16-column blocks).
+// A decode step (page "sparse_delta_memory/decode.py", docstring of
+// sdm_decode_step) gathers the W written rows of a stream, forms retrieved and
+// delta_v per column, writes the W rows back decayed and updated, and reads the
+// R rows back as a weighted sum after the write. Every quantity is per column,
+// so column slices are independent and a workgroup owns all W and R rows of its
+// stream within its slice: only its own stores can change what its reads see
+// (the same argument as the prior-art Triton kernel on that page, whose
+// programs own 16-column blocks).
 //
 // Layout of a workgroup: RG row groups of LPR lanes. Lane l of row group j
 // holds vector (slice * LPR + l) of rows j, j + RG, j + 2 RG, ... (JN <= 8 rows
 // per phase), so every row is read with 16-byte loads (narrower when a row is
-// not a multiple of 16 bytes) spread over LPR lanes, and the rows stay in
-// registers between the retrieval and the write-back.
+// not a multiple of 16 bytes) spread over LPR lanes, and the W rows stay in
+// registers between the retrieval and the write-back. The per-group partial
+// sums meet in LDS, where one thread per column adds them in group order.
 //
-// Phases: the W rows are requested together, used for the retrieval and
-// written back; then, after a workgroup barrier that orders the write-back
-// before any read, the R rows are requested together into the same registers
-// (a lane holds one phase's rows at a time, which keeps occupancy high) and
-// summed. (Comparing the slot lists to skip that barrier where no read slot is
-// written cost more than it saved.)
+// sdm_decode_kernel (one step): stage the stream's slots and weights in LDS;
+// request all W rows; retrieval, delta_v, write-back; a workgroup barrier
+// (workgroup-scope release/acquire) orders the write-back before the reads;
+// request all R rows into the same registers (one phase's rows at a time keeps
+// occupancy high); readings.
 //
-// The per-group partial sums meet in LDS, where one thread per column adds them
-// in group order. This is an HBM-bound gather/scatter (about 1 flop per byte):
-// vector memory and VALU FMAs, no MFMA.
+// sdm_decode_steps_kernel (T steps of one stream in one launch): the same step
+// in a loop, software-pipelined so each step costs about two memory round trips
+// instead of four plus a launch: right after the barrier that publishes step
+// t's writes, the R rows of step t and the W rows of step t + 1 are requested
+// together (step t + 1's rows may be ones step t wrote, which that barrier
+// orders), and the slots and weights of step t + 2 are fetched into registers
+// while those rows are in flight.
+//
+// This is an HBM-bound gather/scatter (about 1 flop per byte): vector memory
+// and VALU FMAs, no MFMA.
 
 #include "sdm_kernels.h"
 
@@ -34,65 +41,235 @@ namespace {
 
 // Rows a lane holds per phase at most: fixes RG, and with it the summation order.
 constexpr int kRowsPerLane = 4;
-
-struct DecodeLds {
+// One step's staged metadata in LDS.
+struct Stage {
     int64_t* kslot;  // [W]
     int64_t* qslot;  // [R]
     float* kv;       // [W] k_val rounded to the bank dtype
     float* d;        // [W] exp(g)
     float* coef;     // [W] kv * d
     float* qv;       // [R] q_val rounded to the bank dtype
-    float* v;        // [slice_cols] v rounded to the bank dtype
-    float* partial;  // [RG][slice_cols]
-    float* dv;       // [slice_cols]
+    float* v;        // [slice_cols] v rounded to the bank dtype (0 past head_dim)
     float* beta;     // [1]
 };
 
-__device__ __forceinline__ DecodeLds carve(char* base, int W, int R, int rg, int slice_cols) {
-    DecodeLds l;
-    l.kslot = reinterpret_cast<int64_t*>(base);
-    l.qslot = l.kslot + W;
-    float* f = reinterpret_cast<float*>(l.qslot + R);
-    l.kv = f;
-    l.d = l.kv + W;
-    l.coef = l.d + W;
-    l.qv = l.coef + W;
-    l.v = l.qv + R;
-    l.partial = l.v + slice_cols;
-    l.dv = l.partial + rg * slice_cols;
-    l.beta = l.dv + slice_cols;
-    return l;
+__device__ __host__ __forceinline__ size_t stage_bytes(int W, int R, int slice_cols) {
+    const size_t b = size_t(8) * (W + R) + size_t(4) * (3 * W + R + slice_cols + 1);
+    return (b + 15) & ~size_t(15);
 }
 
-// Stage stream s's slots, rounded weights, decays, v (this slice) and beta in LDS.
-template <typename E, typename KI, typename QI, typename VT>
-__device__ __forceinline__ void stage(const DecodeParams& p, const DecodeLds& L, int64_t s, int64_t col0,
-                                      int slice_cols) {
+__device__ __forceinline__ Stage carve_stage(char* base, int W, int R, int slice_cols) {
+    Stage st;
+    st.kslot = reinterpret_cast<int64_t*>(base);
+    st.qslot = st.kslot + W;
+    st.kv = reinterpret_cast<float*>(st.qslot + R);
+    st.d = st.kv + W;
+    st.coef = st.d + W;
+    st.qv = st.coef + W;
+    st.v = st.qv + R;
+    st.beta = st.v + slice_cols;
+    return st;
+}
+
+// Stage stream s's metadata of step t directly (loads, then LDS stores).
+template <typename E>
+__device__ __forceinline__ void stage_direct(const DecodeParams& p, int t, int64_t s, const Stage& st, int64_t col0,
+                                             int slice_cols) {
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const KI* k_idx = static_cast<const KI*>(p.k_idx);
-    const QI* q_idx = static_cast<const QI*>(p.q_idx);
-    const VT* k_val = static_cast<const VT*>(p.k_val);
-    const VT* q_val = static_cast<const VT*>(p.q_val);
-    const VT* v = static_cast<const VT*>(p.v);
+    const int64_t row = int64_t(t) * p.streams + s;  // this stream's row of step t
     for (int i = tid; i < p.W; i += nthr) {
-        const int64_t at = s * p.W + i;
-        const float kv = to_bank<E>(value_of<VT>(k_val[at]));
-        const float d = float(exp(double(p.g[s * p.G + (p.G == 1 ? 0 : i)])));
-        L.kslot[i] = int64_t(k_idx[at]);
-        L.kv[i] = kv;
-        L.d[i] = d;
-        L.coef[i] = kv * d;
+        const float kv = to_bank<E>(value_at(p.k_val, row * p.W + i, p.val_bytes));
+        const float d = float(exp(double(p.g[row * p.G + (p.G == 1 ? 0 : i)])));
+        st.kslot[i] = slot_at(p.k_idx, row * p.W + i, p.k_bytes);
+        st.kv[i] = kv;
+        st.d[i] = d;
+        st.coef[i] = kv * d;
     }
     for (int i = tid; i < p.R; i += nthr) {
-        const int64_t at = s * p.R + i;
-        L.qslot[i] = int64_t(q_idx[at]);
-        L.qv[i] = to_bank<E>(value_of<VT>(q_val[at]));
+        st.qslot[i] = slot_at(p.q_idx, row * p.R + i, p.q_bytes);
+        st.qv[i] = to_bank<E>(value_at(p.q_val, row * p.R + i, p.val_bytes));
     }
     for (int col = tid; col < slice_cols; col += nthr) {
         const int64_t c = col0 + col;
-        L.v[col] = c < p.hd ? to_bank<E>(value_of<VT>(v[s * p.hd + c])) : 0.0f;
+        st.v[col] = c < p.hd ? to_bank<E>(value_at(p.v, row * p.hd + c, p.val_bytes)) : 0.0f;
     }
-    if (tid == 0) L.beta[0] = p.beta[s];
+    if (tid == 0) st.beta[0] = p.beta[row];
+}
+
+// A step's metadata as fetched ahead by one thread, into registers: items
+// i = tid + m * threads, MK of W and R and MV of the slice's v. Every load is
+// unconditional (indices clamped to the last item), so no load sits in a
+// guarded block where the compiler would wait for it.
+template <int MK, int MV>
+struct Meta {
+    int64_t ks[MK], qs[MK];
+    float kraw[MK], graw[MK], qraw[MK], vraw[MV];
+    float beta;
+};
+
+template <int MK, int MV>
+__device__ __forceinline__ void meta_load(const DecodeParams& p, int t, int64_t s, int64_t col0, Meta<MK, MV>& m) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int64_t row = int64_t(t) * p.streams + s;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+        const int i = min(tid + k * nthr, p.W - 1);
+        m.ks[k] = slot_at(p.k_idx, row * p.W + i, p.k_bytes);
+        m.kraw[k] = value_at(p.k_val, row * p.W + i, p.val_bytes);
+        m.graw[k] = p.g[row * p.G + (p.G == 1 ? 0 : i)];
+        const int r = min(tid + k * nthr, p.R - 1);
+        m.qs[k] = slot_at(p.q_idx, row * p.R + r, p.q_bytes);
+        m.qraw[k] = value_at(p.q_val, row * p.R + r, p.val_bytes);
+    }
+#pragma unroll
+    for (int k = 0; k < MV; ++k) {
+        const int64_t c = min(col0 + tid + k * nthr, p.hd - 1);
+        m.vraw[k] = value_at(p.v, row * p.hd + c, p.val_bytes);
+    }
+    m.beta = p.beta[row];
+}
+
+// Round fetched metadata to the bank dtype, form decays and coefficients, and
+// store it in a Stage.
+template <typename E, int MK, int MV>
+__device__ __forceinline__ void meta_store(const DecodeParams& p, const Meta<MK, MV>& m, const Stage& st,
+                                           int64_t col0, int slice_cols) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+        const int i = tid + k * nthr;
+        if (i < p.W) {
+            const float kv = to_bank<E>(m.kraw[k]);
+            const float d = float(exp(double(m.graw[k])));
+            st.kslot[i] = m.ks[k];
+            st.kv[i] = kv;
+            st.d[i] = d;
+            st.coef[i] = kv * d;
+        }
+        if (i < p.R) {
+            st.qslot[i] = m.qs[k];
+            st.qv[i] = to_bank<E>(m.qraw[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < MV; ++k) {
+        const int col = tid + k * nthr;
+        if (col < slice_cols) st.v[col] = col0 + col < p.hd ? to_bank<E>(m.vraw[k]) : 0.0f;
+    }
+    if (tid == 0) st.beta[0] = m.beta;
+}
+
+// Lane geometry shared by the phases.
+struct Lane {
+    int grp, lane, vi, slice_cols;
+    bool active;   // the lane's vector lies inside the row
+    int64_t vcol;  // element offset of the lane's vector (clamped for inactive lanes)
+    int64_t col0;  // first column of the slice
+};
+
+// Request rows slots[j * RG + grp] (j < JN) of the bank, all before any is used.
+// Rows past n re-read row n - 1 and are ignored.
+template <typename E, int VB, int JN>
+__device__ __forceinline__ void load_rows(typename RawVec<VB>::T (&row)[JN], const E* bank, const int64_t* slots,
+                                          int n, int rg, int64_t hd, const Lane& ln) {
+    using V = typename RawVec<VB>::T;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+        const int w = ln.grp + j * rg;
+        row[j] = *reinterpret_cast<const V*>(bank + slots[w < n ? w : n - 1] * hd + ln.vcol);
+    }
+}
+
+// This lane's partial of sum_w weight[w] * row_w over its rows, ascending, into
+// partial[grp][lane's columns].
+template <typename E, int VB, int JN>
+__device__ __forceinline__ void row_partials(const typename RawVec<VB>::T (&row)[JN], const float* weight, int n,
+                                             int rg, const Lane& ln, float* partial) {
+    constexpr int VEC = VB / int(sizeof(E));
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+        const int w = ln.grp + j * rg;
+        if (ln.active && w < n) {
+            E el[VEC];
+            __builtin_memcpy(el, &row[j], VB);
+            const float c = weight[w];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(c, widen(el[e]), acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) partial[ln.grp * ln.slice_cols + ln.lane * VEC + e] = acc[e];
+}
+
+// Column col's total over the row groups, in group order from +0.
+__device__ __forceinline__ float column_total(const float* partial, int rg, int slice_cols, int col) {
+    float total = 0.0f;
+    for (int j = 0; j < rg; ++j) total += partial[j * slice_cols + col];
+    return total;
+}
+
+// delta_v = beta (v - retrieved) per column of the slice.
+__device__ __forceinline__ void form_delta(const DecodeParams& p, const Stage& st, const float* partial, float* dv,
+                                          const Lane& ln) {
+    for (int col = threadIdx.x; col < ln.slice_cols; col += blockDim.x)
+        if (ln.col0 + col < p.hd) dv[col] = st.beta[0] * (st.v[col] - column_total(partial, p.rg, ln.slice_cols, col));
+}
+
+// Decay-and-write of the W rows this lane holds. Write slots are distinct within
+// a stream, so plain stores suffice. opaque() hides the raw bits from the
+// optimiser, so the rows are widened again here instead of being kept widened
+// (twice the registers for bfloat16) across the barriers before this point.
+template <typename E, int VB, int JN>
+__device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E* bank, const Stage& st,
+                                           const float* dv, int W, int rg, int64_t hd, const Lane& ln) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+#pragma unroll
+    for (int j = 0; j < JN; ++j) opaque(row[j]);
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+        const int w = ln.grp + j * rg;
+        if (ln.active && w < W) {
+            E el[VEC], out[VEC];
+            __builtin_memcpy(el, &row[j], VB);
+            const float kv = st.kv[w], d = st.d[w];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float decayed = widen(el[e]) * d;
+                out[e] = narrow<E>(__builtin_fmaf(kv, dv[ln.lane * VEC + e], decayed));
+            }
+            V o;
+            __builtin_memcpy(&o, out, VB);
+            *reinterpret_cast<V*>(bank + st.kslot[w] * hd + ln.vcol) = o;
+        }
+    }
+}
+
+// readings[row][col] = the column totals, rounded to the bank dtype.
+template <typename E>
+__device__ __forceinline__ void store_readings(const DecodeParams& p, const float* partial, int64_t out_row,
+                                               const Lane& ln) {
+    E* readings = static_cast<E*>(p.readings);
+    for (int col = threadIdx.x; col < ln.slice_cols; col += blockDim.x) {
+        const int64_t c = ln.col0 + col;
+        if (c < p.hd) readings[out_row * p.hd + c] = narrow<E>(column_total(partial, p.rg, ln.slice_cols, col));
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ Lane lane_geometry(const DecodeParams& p) {
+    Lane ln;
+    ln.lane = threadIdx.x & (p.lpr - 1);
+    ln.grp = threadIdx.x / p.lpr;
+    ln.slice_cols = p.lpr * VEC;
+    ln.vi = int(blockIdx.y) * p.lpr + ln.lane;
+    ln.active = ln.vi < p.vpr;
+    ln.vcol = int64_t(ln.active ? ln.vi : p.vpr - 1) * VEC;
+    ln.col0 = int64_t(blockIdx.y) * ln.slice_cols;
+    return ln;
 }
 
 // JN: rows a lane holds per phase (a power of two >= ceil(max(W, R) / RG)).
@@ -101,148 +278,111 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
     extern __shared__ __align__(16) char s_raw[];
-
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int lane = tid & (p.lpr - 1);
-    const int grp = tid / p.lpr;
+    const Lane ln = lane_geometry<VEC>(p);
     const int64_t s = blockIdx.x;
-    const int slice_cols = p.lpr * VEC;
-    const int vi = int(blockIdx.y) * p.lpr + lane;
-    const bool active = vi < p.vpr;
-    const int64_t col0 = int64_t(blockIdx.y) * slice_cols;
-    const DecodeLds L = carve(s_raw, p.W, p.R, p.rg, slice_cols);
+    const Stage st = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
+    float* partial = reinterpret_cast<float*>(s_raw + stage_bytes(p.W, p.R, ln.slice_cols));
+    float* dv = partial + p.rg * ln.slice_cols;
     E* bank = static_cast<E*>(p.bank);
 
-    // ---- the stream's slots, weights (rounded to the bank dtype), decays, v.
-    // One branch-free copy per (index types, value type): all of a thread's
-    // loads are issued together.
-    switch (p.k64 | (p.q64 << 1) | (p.val_bf16 << 2)) {
-        case 0: stage<E, int32_t, int32_t, float>(p, L, s, col0, slice_cols); break;
-        case 1: stage<E, int64_t, int32_t, float>(p, L, s, col0, slice_cols); break;
-        case 2: stage<E, int32_t, int64_t, float>(p, L, s, col0, slice_cols); break;
-        case 3: stage<E, int64_t, int64_t, float>(p, L, s, col0, slice_cols); break;
-        case 4: stage<E, int32_t, int32_t, uint16_t>(p, L, s, col0, slice_cols); break;
-        case 5: stage<E, int64_t, int32_t, uint16_t>(p, L, s, col0, slice_cols); break;
-        case 6: stage<E, int32_t, int64_t, uint16_t>(p, L, s, col0, slice_cols); break;
-        default: stage<E, int64_t, int64_t, uint16_t>(p, L, s, col0, slice_cols); break;
-    }
+    stage_direct<E>(p, 0, s, st, ln.col0, ln.slice_cols);
     __syncthreads();
 
-    // ---- request every W row before using any. The loads are unconditional: a
-    // lane past the row end or a row past W reads a clamped address (a line the
-    // wavefront fetches anyway) and ignores it. Guarded loads would let the
-    // compiler wait for each row next to its load.
-    const int64_t vcol = int64_t(active ? vi : p.vpr - 1) * VEC;
     V row[JN];
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int w = grp + j * p.rg;
-        row[j] = *reinterpret_cast<const V*>(bank + L.kslot[w < p.W ? w : p.W - 1] * p.hd + vcol);
-    }
-
-    // ---- retrieval partials, in ascending w within the row group.
-    float acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int w = grp + j * p.rg;
-        if (active && w < p.W) {
-            E el[VEC];
-            __builtin_memcpy(el, &row[j], VB);
-            const float c = L.coef[w];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(c, widen(el[e]), acc[e]);
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) L.partial[grp * slice_cols + lane * VEC + e] = acc[e];
+    load_rows<E, VB, JN>(row, bank, st.kslot, p.W, p.rg, p.hd, ln);
+    row_partials<E, VB, JN>(row, st.coef, p.W, p.rg, ln, partial);
     __syncthreads();
+    form_delta(p, st, partial, dv, ln);
+    __syncthreads();
+    write_back<E, VB, JN>(row, bank, st, dv, p.W, p.rg, p.hd, ln);
 
-    // retrieved (group partials in group order) and delta_v, one thread per column.
-    for (int col = tid; col < slice_cols; col += nthr) {
-        if (col0 + col < p.hd) {
-            float total = 0.0f;
-            for (int j = 0; j < p.rg; ++j) total += L.partial[j * slice_cols + col];
-            L.dv[col] = L.beta[0] * (L.v[col] - total);
-        }
+    // Ordering point: the write-back is visible to the loads below, for read slots
+    // that are also write slots. No other workgroup touches these columns of
+    // these slots.
+    __syncthreads();
+    load_rows<E, VB, JN>(row, bank, st.qslot, p.R, p.rg, p.hd, ln);
+    // The write phase's partials were last read before the barrier preceding the
+    // write-back, so they can be overwritten now.
+    row_partials<E, VB, JN>(row, st.qv, p.R, p.rg, ln, partial);
+    __syncthreads();
+    store_readings<E>(p, partial, s, ln);
+}
+
+// MK, MV: metadata items per thread fetched ahead (W, R <= MK threads; the
+// slice's columns <= MV threads).
+template <typename E, int VB, int JN, int MK, int MV>
+__global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodeParams p) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+    extern __shared__ __align__(16) char s_raw[];
+    const Lane ln = lane_geometry<VEC>(p);
+    const int64_t s = blockIdx.x;
+    const size_t sb = stage_bytes(p.W, p.R, ln.slice_cols);  // two Stage buffers, alternating by step
+    float* partial = reinterpret_cast<float*>(s_raw + 2 * sb);
+    float* dv = partial + p.rg * ln.slice_cols;
+    E* bank = static_cast<E*>(p.bank);
+    const int T = p.steps;
+
+    {
+        const Stage st0 = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
+        stage_direct<E>(p, 0, s, st0, ln.col0, ln.slice_cols);
     }
     __syncthreads();
+    V wrow[JN], rrow[JN];
+    load_rows<E, VB, JN>(wrow, bank, carve_stage(s_raw, p.W, p.R, ln.slice_cols).kslot, p.W, p.rg, p.hd, ln);
+    Meta<MK, MV> m;
+    meta_load(p, min(1, T - 1), s, ln.col0, m);
 
-    // ---- decay-and-write of the rows this lane holds. Write slots are distinct
-    // within a stream, so plain stores suffice. opaque() hides the raw bits from
-    // the optimiser, so the rows are widened again here instead of being kept
-    // widened (twice the registers for bfloat16) across the two barriers above.
-#pragma unroll
-    for (int j = 0; j < JN; ++j) opaque(row[j]);
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int w = grp + j * p.rg;
-        if (active && w < p.W) {
-            E el[VEC], out[VEC];
-            __builtin_memcpy(el, &row[j], VB);
-            const float kv = L.kv[w], d = L.d[w];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float decayed = widen(el[e]) * d;
-                out[e] = narrow<E>(__builtin_fmaf(kv, L.dv[lane * VEC + e], decayed));
-            }
-            V o;
-            __builtin_memcpy(&o, out, VB);
-            *reinterpret_cast<V*>(bank + L.kslot[w] * p.hd + int64_t(vi) * VEC) = o;
+    for (int t = 0; t < T; ++t) {
+        const Stage st = carve_stage(s_raw + (t & 1) * sb, p.W, p.R, ln.slice_cols);
+        const Stage nx = carve_stage(s_raw + ((t + 1) & 1) * sb, p.W, p.R, ln.slice_cols);
+        // step t: retrieval, delta_v, write-back.
+        row_partials<E, VB, JN>(wrow, st.coef, p.W, p.rg, ln, partial);
+        __syncthreads();
+        form_delta(p, st, partial, dv, ln);
+        __syncthreads();
+        write_back<E, VB, JN>(wrow, bank, st, dv, p.W, p.rg, p.hd, ln);
+        // step t + 1's metadata (fetched during step t - 1) into the other buffer,
+        // whose last reader (step t - 1's readings) finished before the barrier
+        // that ended step t - 1.
+        if (t + 1 < T) meta_store<E, MK, MV>(p, m, nx, ln.col0, ln.slice_cols);
+        // Ordering point: step t's write-back is visible to every load below (step
+        // t's reads and step t + 1's writes), and step t + 1's metadata is staged.
+        __syncthreads();
+        load_rows<E, VB, JN>(rrow, bank, st.qslot, p.R, p.rg, p.hd, ln);
+        if (t + 1 < T) {
+            load_rows<E, VB, JN>(wrow, bank, nx.kslot, p.W, p.rg, p.hd, ln);
+            meta_load(p, min(t + 2, T - 1), s, ln.col0, m);
         }
-    }
-
-    // ---- ordering point: the barrier (workgroup-scope release/acquire) makes
-    // the stores above visible to the loads below, for read slots that are also
-    // write slots. No other workgroup touches these columns of these slots.
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int r = grp + j * p.rg;
-        row[j] = *reinterpret_cast<const V*>(bank + L.qslot[r < p.R ? r : p.R - 1] * p.hd + vcol);
-    }
-
-    // ---- readings: weighted sum of the R rows as stored, in group order.
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        const int r = grp + j * p.rg;
-        if (active && r < p.R) {
-            E el[VEC];
-            __builtin_memcpy(el, &row[j], VB);
-            const float q = L.qv[r];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(q, widen(el[e]), acc[e]);
-        }
-    }
-    // The partials of the write phase were last read before the barrier that
-    // preceded the write-back, so they can be overwritten now.
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) L.partial[grp * slice_cols + lane * VEC + e] = acc[e];
-    __syncthreads();
-    E* readings = static_cast<E*>(p.readings);
-    for (int col = tid; col < slice_cols; col += nthr) {
-        const int64_t c = col0 + col;
-        if (c < p.hd) {
-            float total = 0.0f;
-            for (int j = 0; j < p.rg; ++j) total += L.partial[j * slice_cols + col];
-            readings[s * p.hd + c] = narrow<E>(total);
-        }
+        // step t: readings.
+        row_partials<E, VB, JN>(rrow, st.qv, p.R, p.rg, ln, partial);
+        __syncthreads();
+        store_readings<E>(p, partial, int64_t(t) * p.streams + s, ln);
+        // partial and this step's buffer are free once every thread is past here.
+        __syncthreads();
     }
 }
 
-template <typename E, int VB>
-hipError_t launch_vb(const DecodeParams& p, const DecodeGeometry& geo, int64_t streams, hipStream_t stream) {
-    const dim3 grid(unsigned(streams), unsigned(geo.slices));
+template <typename E, int VB, int JN>
+void launch_jn(const DecodeParams& p, const DecodeGeometry& geo, hipStream_t stream) {
+    const dim3 grid(unsigned(p.streams), unsigned(geo.slices));
     const dim3 block(unsigned(geo.threads));
+    const int slice_cols = geo.lpr * (VB / int(sizeof(E)));
+    if (p.steps == 1)
+        hipLaunchKernelGGL((sdm_decode_kernel<E, VB, JN>), grid, block, geo.lds, stream, p);
+    else if (p.W <= geo.threads && p.R <= geo.threads && slice_cols <= geo.threads)
+        hipLaunchKernelGGL((sdm_decode_steps_kernel<E, VB, JN, 1, 1>), grid, block, geo.lds, stream, p);
+    else
+        hipLaunchKernelGGL((sdm_decode_steps_kernel<E, VB, JN, 4, 8>), grid, block, geo.lds, stream, p);
+}
+
+template <typename E, int VB>
+hipError_t launch_vb(const DecodeParams& p, const DecodeGeometry& geo, hipStream_t stream) {
     switch (geo.jn) {
-        case 1: hipLaunchKernelGGL((sdm_decode_kernel<E, VB, 1>), grid, block, geo.lds, stream, p); break;
-        case 2: hipLaunchKernelGGL((sdm_decode_kernel<E, VB, 2>), grid, block, geo.lds, stream, p); break;
-        case 4: hipLaunchKernelGGL((sdm_decode_kernel<E, VB, 4>), grid, block, geo.lds, stream, p); break;
-        default: hipLaunchKernelGGL((sdm_decode_kernel<E, VB, 8>), grid, block, geo.lds, stream, p); break;
+        case 1: launch_jn<E, VB, 1>(p, geo, stream); break;
+        case 2: launch_jn<E, VB, 2>(p, geo, stream); break;
+        case 4: launch_jn<E, VB, 4>(p, geo, stream); break;
+        default: launch_jn<E, VB, 8>(p, geo, stream); break;
     }
     return hipGetLastError();
 }
@@ -255,7 +395,7 @@ int pow2_ceil(int64_t x) {
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr) {
+DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, bool multi_step) {
     DecodeGeometry g{};
     const int64_t row_bytes = hd * es;
     g.vb = es;
@@ -272,29 +412,33 @@ DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_
     g.rg = pow2_ceil((wmax + kRowsPerLane - 1) / kRowsPerLane);
     if (g.rg > 32) g.rg = 32;
     g.jn = pow2_ceil((wmax + g.rg - 1) / g.rg);
+    // A thread fetches at most 4 slots of W and of R ahead of a step (8 elements
+    // of v are covered by any lane group): widen the lane group (extra lanes past
+    // the row end are idle) where that would not cover them. RG, and with it the
+    // summation order, stays as it is.
+    while (g.lpr * g.rg * 4 < wmax) g.lpr *= 2;
+    g.slices = (g.vpr + g.lpr - 1) / g.lpr;
     g.threads = g.lpr * g.rg;
     const int slice_cols = g.lpr * (g.vb / es);
-    // kslot, qslot (8 B each); kv, d, coef, qv (4 B); v, partial, dv; beta
-    g.lds = size_t(8) * (W + R) + size_t(4) * (3 * W + R) +
-            size_t(4) * (size_t(slice_cols) * (g.rg + 2) + 1);
-    g.lds = (g.lds + 15) & ~size_t(15);
+    // one (or two) staging buffers, then partial [RG][slice] and delta_v [slice]
+    g.lds = (multi_step ? 2 : 1) * stage_bytes(W, R, slice_cols) +
+            size_t(4) * size_t(slice_cols) * size_t(g.rg + 1);
     return g;
 }
 
-hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, int64_t streams, bool bf16,
-                         hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, bool bf16, hipStream_t stream) {
     if (bf16) {
         switch (geo.vb) {
-            case 16: return launch_vb<uint16_t, 16>(p, geo, streams, stream);
-            case 8: return launch_vb<uint16_t, 8>(p, geo, streams, stream);
-            case 4: return launch_vb<uint16_t, 4>(p, geo, streams, stream);
-            default: return launch_vb<uint16_t, 2>(p, geo, streams, stream);
+            case 16: return launch_vb<uint16_t, 16>(p, geo, stream);
+            case 8: return launch_vb<uint16_t, 8>(p, geo, stream);
+            case 4: return launch_vb<uint16_t, 4>(p, geo, stream);
+            default: return launch_vb<uint16_t, 2>(p, geo, stream);
         }
     }
     switch (geo.vb) {
-        case 16: return launch_vb<float, 16>(p, geo, streams, stream);
-        case 8: return launch_vb<float, 8>(p, geo, streams, stream);
-        default: return launch_vb<float, 4>(p, geo, streams, stream);
+        case 16: return launch_vb<float, 16>(p, geo, stream);
+        case 8: return launch_vb<float, 8>(p, geo, stream);
+        default: return launch_vb<float, 4>(p, geo, stream);
     }
 }
 

@@ -51,6 +51,30 @@ template <> __device__ __forceinline__ float narrow<float>(float f) { return f; 
 // Round a float32 to the bank element type and widen it back.
 template <typename E> __device__ __forceinline__ float to_bank(float f) { return widen(narrow<E>(f)); }
 
+// A slot of an int32 (idx_bytes = 4) or int64 (8) array, with no branch on the
+// type: two 32-bit loads, at the same address for int32, always both consumed
+// (through a mask), so the compiler cannot move one of them under a branch and
+// wait for it there.
+__device__ __forceinline__ int64_t slot_at(const void* base, int64_t i, int idx_bytes) {
+    const char* q = static_cast<const char*>(base) + i * idx_bytes;
+    const uint32_t lo = *reinterpret_cast<const uint32_t*>(q);
+    const uint32_t hi = *reinterpret_cast<const uint32_t*>(q + (idx_bytes - 4));
+    const uint32_t wide = 0u - uint32_t(idx_bytes == 8);  // all ones for int64
+    const uint32_t sign = uint32_t(int32_t(lo) >> 31);    // sign extension of an int32
+    return int64_t((uint64_t((hi & wide) | (sign & ~wide)) << 32) | lo);
+}
+
+// A float32 (val_bytes = 4) or bfloat16 (2) value as float32, with no branch on
+// the type: two 16-bit loads (little-endian halves), at the same address for
+// bfloat16, whose bits are the high half of a float32; both always consumed.
+__device__ __forceinline__ float value_at(const void* base, int64_t i, int val_bytes) {
+    const char* q = static_cast<const char*>(base) + i * val_bytes;
+    const uint32_t hi = *reinterpret_cast<const uint16_t*>(q + (val_bytes - 2));
+    const uint32_t lo = *reinterpret_cast<const uint16_t*>(q);
+    const uint32_t keep = 0u - uint32_t(val_bytes == 4);  // all ones for float32
+    return __uint_as_float((hi << 16) | (lo & keep));
+}
+
 // A value or weight given as float32 or bfloat16 (raw bits), as float32.
 template <typename T> __device__ __forceinline__ float value_of(T x);
 template <> __device__ __forceinline__ float value_of<float>(float x) { return x; }
@@ -68,11 +92,13 @@ struct DecodeParams {
     const float* g;
     void* readings;
     int64_t hd;
+    int64_t streams;  // streams per step (the per-step stride of every input)
+    int steps;        // tokens per stream in this call (1 for sdm_decode_step)
     int W, R, G;
     int vpr;  // vectors per row
     int lpr;  // lanes per row group: a power of two <= 32
     int rg;   // row groups
-    int k64, q64, val_bf16;
+    int k_bytes, q_bytes, val_bytes;  // element sizes of k_idx, q_idx and the values
 };
 
 struct DecodeGeometry {
@@ -86,9 +112,8 @@ struct DecodeGeometry {
     size_t lds;  // dynamic LDS bytes
 };
 
-DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr);
-hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, int64_t streams, bool bf16,
-                         hipStream_t stream);
+DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, bool multi_step);
+hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, bool bf16, hipStream_t stream);
 
 // ------------------------------------------------------------------ gather
 struct GatherParams {

@@ -140,3 +140,18 @@ def decode_tolerance_ok(x: np.ndarray, ref: np.ndarray, mag: np.ndarray, bf16: b
     err = np.abs(x - ref)
     ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1), np.where(err > 0, np.inf, 0))
     return bool(np.all(err <= bound)), float(ratio.max(initial=0.0))
+
+
+def sub_inputs(inp: dict, streams: np.ndarray, P: int) -> dict:
+    """One step's numpy inputs of the given streams, slots renumbered into the
+    concatenation of those streams' private ranges (P slots each)."""
+    out = {k: v[streams] for k, v in inp.items()}
+    shift = (streams.astype(np.int64) * P - np.arange(len(streams), dtype=np.int64) * P)[:, None]
+    out["k_idx"] = out["k_idx"] - shift
+    out["q_idx"] = out["q_idx"] - shift
+    return out
+
+
+def stream_rows(streams: np.ndarray, P: int) -> np.ndarray:
+    """Bank rows of the given streams' private ranges, concatenated."""
+    return (np.asarray(streams)[:, None].astype(np.int64) * P + np.arange(P)[None, :]).ravel()

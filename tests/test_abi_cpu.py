@@ -31,8 +31,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_gather",
-                                     "sdm_last_error"]
+    assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_decode_steps",
+                                     "sdm_gather", "sdm_last_error"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,6 +107,37 @@ def test_decode_rejects(kw, code, text):
 
 def test_decode_zero_streams_is_a_no_op():
     rc, msg = call_decode(streams=0, bank=None, readings=None)
+    assert rc == OK and msg == ""
+
+
+def call_decode_steps(steps, **kw):
+    a = decode_args(**kw)
+    lib = sdm.library()
+    rc = lib.sdm_decode_steps(a["bank"], a["bank_dtype"], a["num_slots"], a["head_dim"], steps, a["streams"],
+                              a["W"], a["R"], a["G"], a["k_idx"], a["k_idx_dtype"], a["k_val"], a["v"],
+                              a["q_val"], a["val_dtype"], a["beta"], a["g"], a["q_idx"], a["q_idx_dtype"],
+                              a["readings"], a["stream"])
+    return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("steps,kw,code,text", [
+    (-1, {}, E_SHAPE, "steps = -1"),
+    (4, dict(W=0), E_RANGE, "W and R"),
+    (4, dict(G=3), E_SHAPE, "G must be 1 or W"),
+    (4, dict(v=None), E_NULL, "v is NULL"),
+    (4, dict(q_val=A + 1300 * MB + 2, val_dtype=F32), E_ALIGN, "aligned"),
+    # readings [4, 8, 128] bf16 end 2 bytes into the bank
+    (4, dict(readings=A - 4 * 8 * 128 * 2 + 2), E_OVERLAP, "overlap"),
+    (1 << 40, dict(streams=1 << 20), E_SHAPE, "overflow"),
+])
+def test_decode_steps_rejects(steps, kw, code, text):
+    rc, msg = call_decode_steps(steps, **kw)
+    assert rc == code, msg
+    assert text in msg and msg.startswith("sdm_decode_steps")
+
+
+def test_decode_steps_zero_steps_is_a_no_op():
+    rc, msg = call_decode_steps(0, bank=None, readings=None)
     assert rc == OK and msg == ""
 
 

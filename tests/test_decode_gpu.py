@@ -20,7 +20,7 @@ import gen
 import oracle
 from sparse_delta_rule_amd import sdm_decode_step
 from tests.helpers import (bits_equal, decode_tolerance_ok, documented_decode_groups, from_np_bank,
-                           step_to_numpy, to_np_bank)
+                           step_to_numpy, stream_rows, sub_inputs, to_np_bank)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -28,19 +28,6 @@ DEV = torch.device("cuda", 0)
 
 def _say(*a):
     print(*a, flush=True)
-
-
-def _sub_inputs(inp: dict, streams: np.ndarray, P: int) -> dict:
-    """Inputs of the given streams, slots renumbered into their concatenated ranges."""
-    out = {k: v[streams] for k, v in inp.items()}
-    shift = (streams.astype(np.int64) * P - np.arange(len(streams), dtype=np.int64) * P)[:, None]
-    out["k_idx"] = out["k_idx"] - shift
-    out["q_idx"] = out["q_idx"] - shift
-    return out
-
-
-def _ranges(streams: np.ndarray, P: int) -> np.ndarray:
-    return (streams[:, None].astype(np.int64) * P + np.arange(P)[None, :]).ravel()
 
 
 def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, device_inputs=False,
@@ -54,8 +41,8 @@ def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, 
     free_streams = np.asarray(free_streams, dtype=np.int64)
     sync_streams = np.asarray(sync_streams, dtype=np.int64)
     assert not set(free_streams) & set(sync_streams)
-    free_rows = torch.from_numpy(_ranges(free_streams, P)).to(DEV)
-    sync_rows = torch.from_numpy(_ranges(sync_streams, P)).to(DEV)
+    free_rows = torch.from_numpy(stream_rows(free_streams, P)).to(DEV)
+    sync_rows = torch.from_numpy(stream_rows(sync_streams, P)).to(DEV)
     bank_free = to_np_bank(bank[free_rows])      # oracle, kernel order, free-running
     bank_sync = to_np_bank(bank[sync_rows])      # oracle, ascending order, resynced into the GPU
     rg = documented_decode_groups(wl.W, wl.R)
@@ -71,13 +58,13 @@ def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, 
         torch.cuda.synchronize()
         # free-running streams: bit for bit against the kernel's documented order
         if len(free_streams):
-            sub = _sub_inputs(npin, free_streams, P)
+            sub = sub_inputs(npin, free_streams, P)
             ref = oracle.decode_step(bank_free, **sub, groups=rg)
             got = to_np_bank(readings[torch.from_numpy(free_streams).to(DEV)])
             assert bits_equal(got, ref), f"step {t}: readings differ from the oracle (RG={rg})"
         # resynced streams: stated tolerance against the ascending order
         if len(sync_streams):
-            sub = _sub_inputs(npin, sync_streams, P)
+            sub = sub_inputs(npin, sync_streams, P)
             _, _, row_mag, _, read_mag = oracle.decode_step_f64(bank_sync.copy(), **sub)
             before = bank_sync.copy()
             ref = oracle.decode_step(bank_sync, **sub, groups=1)
