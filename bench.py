@@ -74,6 +74,9 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    p.add_argument("--ingest-profile", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="summarise rocprofv3 output directories of this config into profiles/ (no GPU)")
+    p.add_argument("--profile-commands", default="", help="text of the commands that made the directories")
     return p.parse_args(argv)
 
 
@@ -275,8 +278,100 @@ def calibrate_copy(torch):
                       "gbps": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
 
 
+# ------------------------------------------------------------------ profiles
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise SystemExit(f"bench.py: no *{suffix} under {directory}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_kib(directory: str, name_part: str, min_kib: float = 0.0):
+    """Median per-dispatch counter value (KiB) of the kernels whose name contains name_part."""
+    import statistics
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(directory, "counter_collection.csv")
+            if name_part in r["Kernel_Name"] and float(r["Counter_Value"]) >= min_kib]
+    if not vals:
+        raise SystemExit(f"bench.py: no {name_part} dispatches in {directory}")
+    return statistics.median(vals), len(vals)
+
+
+def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
+    """(bytes per launch, unit description) of the row traffic the method needs."""
+    import gen
+    import torch
+    wl = gen.WORKLOADS[cfg_name]
+    es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    if isinstance(wl, gen.DecodeWorkload):
+        per = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
+        tokens = wl.steps if entry == "steps" else 1
+        return per * tokens, f"{tokens} token(s) x {wl.streams} streams x (2W+R)={2 * wl.W + wl.R} rows x {wl.head_dim * es} B"
+    t = torch.arange(wl.tokens)
+    inp = gen.gather_inputs(wl, 0)
+    live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
+    rows = live * (wl.width0 + wl.width1) * wl.head_dim * es + wl.tokens * wl.width0 * wl.head_dim * es
+    return rows, f"{live} live tokens x {wl.width0 + wl.width1} rows read + {wl.tokens} x {wl.width0} stash rows, x {wl.head_dim * es} B"
+
+
+def ingest_profile(args) -> int:
+    trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
+    kernel = "sdm_gather_kernel" if args.config == "c3" else (
+        "sdm_decode_steps_kernel" if args.entry == "steps" else "sdm_decode_kernel")
+    stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if kernel in r["Name"]]
+    if not stats:
+        raise SystemExit(f"bench.py: {kernel} not in the kernel trace under {trace}")
+    calls = sum(int(r["Calls"]) for r in stats)
+    avg_ns = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in stats) / calls
+    f_kib, f_n = _counter_kib(fetch, kernel)
+    w_kib, w_n = _counter_kib(write, kernel)
+    gib_kib = float(1 << 20)  # the calibration copy moves 1 GiB each way
+    cf_kib, _ = _counter_kib(copy_fetch, "elementwise", min_kib=gib_kib / 8)
+    cw_kib, _ = _counter_kib(copy_write, "elementwise", min_kib=gib_kib / 8)
+    f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
+    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    alg, alg_desc = algorithmic_bytes(args.config, args.entry)
+    traffic_path = os.path.join(PROFILES, "traffic.json")
+    data = {}
+    if os.path.exists(traffic_path):
+        with open(traffic_path) as f:
+            data = json.load(f)
+    data[f"{args.config}/{kernel}"] = {
+        "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
+        "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    md = os.path.join(PROFILES, f"{kernel}_{args.config}.md")
+    with open(md, "w") as f:
+        f.write(f"# {kernel} on workload {args.config} (MI355X, rocprofv3)\n\n")
+        f.write(f"Kernel sources hash {kernel_source_hash()} (bench.py `kernel_source_hash`).\n\n")
+        f.write("## Commands\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")
+        f.write("## Kernel trace (`--kernel-trace --stats`)\n\n| kernel | calls | average | min | max |\n|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} us | "
+                    f"{float(r['MinNs']) / 1e3:.2f} us | {float(r['MaxNs']) / 1e3:.2f} us |\n")
+        f.write(f"\nAlgorithmic row bytes per launch: {alg / 2**20:.1f} MiB ({alg_desc}); at the average "
+                f"duration that is {alg / avg_ns:.0f} GB/s, {alg / avg_ns / HBM_PEAK_GBPS:.3f} of the 8 TB/s peak.\n\n")
+        f.write("## HBM bytes (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`, one pass each)\n\n")
+        f.write(f"| counter | KiB per dispatch (median of {f_n}/{w_n}) | scale (1 GiB copy) | bytes per launch |\n|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {f_scale:.4f} (copy read {cf_kib:.0f} KiB for 1048576) | {fetch_b / 2**20:.1f} MiB |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {w_scale:.4f} (copy wrote {cw_kib:.0f} KiB for 1048576) | {write_b / 2**20:.1f} MiB |\n")
+        f.write(f"\nMeasured HBM traffic {(fetch_b + write_b) / 2**20:.1f} MiB per launch against "
+                f"{alg / 2**20:.1f} MiB of algorithmic row bytes (ratio {(fetch_b + write_b) / alg:.3f}; "
+                "the excess is slots, weights, values and outputs).\n")
+    print(json.dumps({"wrote": [traffic_path, md], "avg_kernel_us": avg_ns / 1e3,
+                      "traffic_MiB": (fetch_b + write_b) / 2**20, "alg_MiB": alg / 2**20}))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.ingest_profile:
+        sys.path.insert(0, ROOT)
+        return ingest_profile(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
