@@ -126,7 +126,16 @@ int sdm_decode_step(void* bank, int bank_dtype, int64_t num_slots, int64_t head_
  * q_idx, q_val [steps, streams, R]; readings [steps, streams, head_dim] (must not
  * overlap the bank). steps >= 0; steps == 0 or streams == 0 enqueues nothing.
  * The preconditions apply to every token (slots of one stream stay private to
- * it across all tokens of the call). Errors: as sdm_decode_step.
+ * it across all tokens of the call). Errors: as sdm_decode_step; SDM_E_HIP also
+ * when the device's compute-unit count cannot be queried, SDM_E_RANGE for an
+ * unknown SDM_STEPS_LOOP value.
+ *
+ * The library runs one of two loops, with identical results: a wide one (every
+ * row of a token in flight at once per wave) where the grid leaves at most two
+ * waves on each SIMD, a compact one (fewer registers, more workgroups per CU)
+ * otherwise. The environment variable SDM_STEPS_LOOP=wide or =compact, read on
+ * every call, pins that choice (wide only where a stream's workgroup has at
+ * most 256 threads); it exists for testing and tuning.
  */
 int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
                      int64_t steps, int64_t streams, int32_t W, int32_t R, int32_t G,

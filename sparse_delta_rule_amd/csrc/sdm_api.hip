@@ -6,6 +6,7 @@
 // host checks), reported as status codes with a thread-local message instead of
 // exceptions. Everything cheap is checked on the host before the first HIP call.
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -18,6 +19,8 @@
 #include "sdm_kernels.h"
 
 namespace {
+
+constexpr int kMaxDevices = 64;  // devices whose compute-unit count is cached
 
 thread_local std::string g_last_error;
 
@@ -69,6 +72,39 @@ bool debug_validate() {
         return (e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0) ? 1 : 0;
     }();
     return on != 0;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus(int* cus) {
+    static std::atomic<int> cache[kMaxDevices];  // 0: not queried yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    int v = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (v <= 0) {
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || v <= 0)
+            return fail(SDM_E_HIP, "cannot query the compute units of device %d: %s", dev, hipGetErrorString(e));
+        if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *cus = v;
+    return SDM_OK;
+}
+
+// SDM_STEPS_LOOP=compact|wide pins the multi-step loop; read on every call.
+int forced_loop(int* loop) {
+    const char* e = std::getenv("SDM_STEPS_LOOP");
+    *loop = -1;
+    if (e == nullptr || e[0] == '\0') return SDM_OK;
+    if (std::strcmp(e, "compact") == 0) {
+        *loop = sdm::kLoopCompact;
+        return SDM_OK;
+    }
+    if (std::strcmp(e, "wide") == 0) {
+        *loop = sdm::kLoopWide;
+        return SDM_OK;
+    }
+    return fail(SDM_E_RANGE, "SDM_STEPS_LOOP is '%s'; expected 'compact' or 'wide'", e);
 }
 
 int check_device_ptr(const void* p, const char* name) {
@@ -230,8 +266,14 @@ int decode_call(const char* fn, void* bank, int bank_dtype, int64_t num_slots, i
         }
     }
 
+    int cus = 0, force = -1;
+    if (steps > 1) {
+        int rc = device_cus(&cus);
+        if (rc == SDM_OK) rc = forced_loop(&force);
+        if (rc != SDM_OK) return rc;
+    }
     const sdm::DecodeGeometry geo =
-        sdm::decode_geometry(es, head_dim, W, R, reinterpret_cast<uintptr_t>(bank), steps > 1);
+        sdm::decode_geometry(es, head_dim, W, R, reinterpret_cast<uintptr_t>(bank), steps, streams, cus, force);
     if (geo.slices > 65535)
         return fail(SDM_E_SHAPE, "%s: head_dim %lld needs %d column slices (max 65535)", fn, (long long)head_dim,
                     geo.slices);

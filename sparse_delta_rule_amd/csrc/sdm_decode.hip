@@ -23,12 +23,12 @@
 // occupancy high); readings.
 //
 // sdm_decode_steps_kernel (T steps of one stream in one launch): the same step
-// in a loop, software-pipelined so each step costs about two memory round trips
-// instead of four plus a launch: right after the barrier that publishes step
-// t's writes, the R rows of step t and the W rows of step t + 1 are requested
-// together (step t + 1's rows may be ones step t wrote, which that barrier
-// orders), and the slots and weights of step t + 2 are fetched into registers
-// while those rows are in flight.
+// in a loop, software-pipelined so each step costs one wait for rows instead of
+// two plus a launch: right after the barrier that publishes step t's writes,
+// the R rows of step t and the W rows of step t + 1 are requested together
+// (both may be rows step t wrote, which that barrier orders), with step t + 2's
+// slots and weights; both weighted sums come out of one pass, and a step takes
+// three workgroup barriers.
 //
 // This is an HBM-bound gather/scatter (about 1 flop per byte): vector memory
 // and VALU FMAs, no MFMA.
@@ -181,7 +181,10 @@ __device__ __forceinline__ void load_rows(typename RawVec<VB>::T (&row)[JN], con
 }
 
 // This lane's partial of sum_w weight[w] * row_w over its rows, ascending, into
-// partial[grp][lane's columns].
+// partial[grp][lane's columns]. Every row is used unconditionally and a select
+// keeps or drops its term (a row used only inside a branch would have its load
+// moved into that branch and waited for there); a dropped term cannot reach the
+// sum, whatever its value.
 template <typename E, int VB, int JN>
 __device__ __forceinline__ void row_partials(const typename RawVec<VB>::T (&row)[JN], const float* weight, int n,
                                              int rg, const Lane& ln, float* partial) {
@@ -192,12 +195,14 @@ __device__ __forceinline__ void row_partials(const typename RawVec<VB>::T (&row)
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
         const int w = ln.grp + j * rg;
-        if (ln.active && w < n) {
-            E el[VEC];
-            __builtin_memcpy(el, &row[j], VB);
-            const float c = weight[w];
+        const bool use = ln.active && w < n;
+        E el[VEC];
+        __builtin_memcpy(el, &row[j], VB);
+        const float c = weight[w < n ? w : n - 1];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(c, widen(el[e]), acc[e]);
+        for (int e = 0; e < VEC; ++e) {
+            const float term = __builtin_fmaf(c, widen(el[e]), acc[e]);
+            acc[e] = use ? term : acc[e];
         }
     }
 #pragma unroll
@@ -310,6 +315,11 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
 
 // MK, MV: metadata items per thread fetched ahead (W, R <= MK threads; the
 // slice's columns <= MV threads).
+//
+// Compact loop, for grids that keep many waves on each SIMD: the write rows of
+// step t + 1 are requested with the read rows of step t, but their sums wait
+// for the next iteration, so fewer values are live at once (at most 128 VGPRs)
+// and more workgroups fit on a CU. Five barriers per step.
 template <typename E, int VB, int JN, int MK, int MV>
 __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodeParams p) {
     using V = typename RawVec<VB>::T;
@@ -363,14 +373,93 @@ __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodePara
     }
 }
 
+// Wide loop, for grids that leave at most two waves on each SIMD, where the
+// memory parallelism has to come from within each wave: iteration t: request the R rows of step t and the W rows of step t + 1 (and
+// step t + 2's metadata) together; one pass forms both partial sums (separate
+// LDS buffers); barrier; readings of step t and delta_v of step t + 1; barrier;
+// write-back of step t + 1 and staging of step t + 2's metadata; barrier (the
+// ordering point for the next iteration's loads). Three barriers per step. Up to
+// 256 threads per workgroup, and the register budget of two waves per SIMD, so
+// the compiler keeps both row sets and the fetched metadata in flight at once
+// instead of trading that for occupancy the grid cannot use.
+template <typename E, int VB, int JN, int MK, int MV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void sdm_decode_steps_wide_kernel(const DecodeParams p) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+    extern __shared__ __align__(16) char s_raw[];
+    const Lane ln = lane_geometry<VEC>(p);
+    const int64_t s = blockIdx.x;
+    const size_t sb = stage_bytes(p.W, p.R, ln.slice_cols);  // two Stage buffers, alternating by step
+    float* wpart = reinterpret_cast<float*>(s_raw + 2 * sb);  // retrieval partials [RG][slice]
+    float* rpart = wpart + p.rg * ln.slice_cols;              // readings partials [RG][slice]
+    float* dv = rpart + p.rg * ln.slice_cols;
+    E* bank = static_cast<E*>(p.bank);
+    const int T = p.steps;
+
+    // step 0's write, alone: stage, request rows, retrieval, delta_v, write-back,
+    // and step 1's metadata into the other buffer.
+    const Stage st0 = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
+    stage_direct<E>(p, 0, s, st0, ln.col0, ln.slice_cols);
+    Meta<MK, MV> m;
+    meta_load(p, min(1, T - 1), s, ln.col0, m);
+    __syncthreads();
+    V wrow[JN], rrow[JN];
+    load_rows<E, VB, JN>(wrow, bank, st0.kslot, p.W, p.rg, p.hd, ln);
+    row_partials<E, VB, JN>(wrow, st0.coef, p.W, p.rg, ln, wpart);
+    __syncthreads();
+    form_delta(p, st0, wpart, dv, ln);
+    __syncthreads();
+    write_back<E, VB, JN>(wrow, bank, st0, dv, p.W, p.rg, p.hd, ln);
+    if (T > 1) meta_store<E, MK, MV>(p, m, carve_stage(s_raw + sb, p.W, p.R, ln.slice_cols), ln.col0,
+                                     ln.slice_cols);
+    __syncthreads();
+
+    for (int t = 0; t < T; ++t) {
+        const Stage st = carve_stage(s_raw + (t & 1) * sb, p.W, p.R, ln.slice_cols);
+        const Stage nx = carve_stage(s_raw + ((t + 1) & 1) * sb, p.W, p.R, ln.slice_cols);
+        const bool more = t + 1 < T;
+        // Step t's writes are visible here (the barrier above); both row sets may
+        // contain slots step t wrote. The load phase has no branch (a guarded load
+        // would be waited for where it is used): after the last step, the rows and
+        // weights of step t's own writes stand in for step t + 1's, and their sums
+        // go unused.
+        const Stage& ws = more ? nx : st;
+        load_rows<E, VB, JN>(rrow, bank, st.qslot, p.R, p.rg, p.hd, ln);
+        load_rows<E, VB, JN>(wrow, bank, ws.kslot, p.W, p.rg, p.hd, ln);
+        meta_load(p, min(t + 2, T - 1), s, ln.col0, m);
+        row_partials<E, VB, JN>(rrow, st.qv, p.R, p.rg, ln, rpart);
+        row_partials<E, VB, JN>(wrow, ws.coef, p.W, p.rg, ln, wpart);
+        __syncthreads();
+        store_readings<E>(p, rpart, int64_t(t) * p.streams + s, ln);
+        if (more) form_delta(p, nx, wpart, dv, ln);
+        __syncthreads();
+        if (more) {
+            write_back<E, VB, JN>(wrow, bank, nx, dv, p.W, p.rg, p.hd, ln);
+            // step t + 2's metadata into this step's buffer, whose last readers (the
+            // loads and partials of step t's reads) finished before the first barrier
+            // of this iteration.
+            if (t + 2 < T) meta_store<E, MK, MV>(p, m, st, ln.col0, ln.slice_cols);
+        }
+        // Ordering point: step t + 1's write-back is visible to the next iteration's
+        // loads, and step t + 2's metadata is staged.
+        __syncthreads();
+    }
+}
+
 template <typename E, int VB, int JN>
 void launch_jn(const DecodeParams& p, const DecodeGeometry& geo, hipStream_t stream) {
     const dim3 grid(unsigned(p.streams), unsigned(geo.slices));
     const dim3 block(unsigned(geo.threads));
     const int slice_cols = geo.lpr * (VB / int(sizeof(E)));
-    if (p.steps == 1)
+    const bool mk1 = p.W <= geo.threads && p.R <= geo.threads && slice_cols <= geo.threads;
+    if (geo.loop == kLoopSingle)
         hipLaunchKernelGGL((sdm_decode_kernel<E, VB, JN>), grid, block, geo.lds, stream, p);
-    else if (p.W <= geo.threads && p.R <= geo.threads && slice_cols <= geo.threads)
+    else if (geo.loop == kLoopWide && mk1)
+        hipLaunchKernelGGL((sdm_decode_steps_wide_kernel<E, VB, JN, 1, 1>), grid, block, geo.lds, stream, p);
+    else if (geo.loop == kLoopWide)
+        hipLaunchKernelGGL((sdm_decode_steps_wide_kernel<E, VB, JN, 4, 8>), grid, block, geo.lds, stream, p);
+    else if (mk1)
         hipLaunchKernelGGL((sdm_decode_steps_kernel<E, VB, JN, 1, 1>), grid, block, geo.lds, stream, p);
     else
         hipLaunchKernelGGL((sdm_decode_steps_kernel<E, VB, JN, 4, 8>), grid, block, geo.lds, stream, p);
@@ -395,7 +484,8 @@ int pow2_ceil(int64_t x) {
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, bool multi_step) {
+DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, int64_t steps,
+                               int64_t streams, int cus, int force_loop) {
     DecodeGeometry g{};
     const int64_t row_bytes = hd * es;
     g.vb = es;
@@ -420,9 +510,23 @@ DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_
     g.slices = (g.vpr + g.lpr - 1) / g.lpr;
     g.threads = g.lpr * g.rg;
     const int slice_cols = g.lpr * (g.vb / es);
-    // one (or two) staging buffers, then partial [RG][slice] and delta_v [slice]
-    g.lds = (multi_step ? 2 : 1) * stage_bytes(W, R, slice_cols) +
-            size_t(4) * size_t(slice_cols) * size_t(g.rg + 1);
+    const size_t stage = stage_bytes(W, R, slice_cols), cols = size_t(4) * size_t(slice_cols);
+    if (steps <= 1) {
+        // one staging buffer, partial [RG][slice] and delta_v [slice]
+        g.loop = kLoopSingle;
+        g.lds = stage + cols * size_t(g.rg + 1);
+        return g;
+    }
+    // waves per SIMD (4 per CU) once the grid is spread over the CUs
+    const int64_t blocks = streams * g.slices, c = cus > 0 ? cus : 1;
+    const int64_t waves_per_block = (g.threads + 63) / 64;
+    const int64_t waves_per_simd = ((blocks + c - 1) / c * waves_per_block + 3) / 4;
+    const bool wide_fits = g.threads <= 256;
+    g.loop = wide_fits && waves_per_simd <= 2 ? kLoopWide : kLoopCompact;
+    if (force_loop == kLoopCompact || (force_loop == kLoopWide && wide_fits)) g.loop = force_loop;
+    // two staging buffers, then one partial buffer (compact) or two (wide), and
+    // delta_v
+    g.lds = 2 * stage + cols * size_t((g.loop == kLoopWide ? 2 : 1) * g.rg + 1);
     return g;
 }
 

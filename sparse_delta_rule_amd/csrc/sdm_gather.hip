@@ -55,7 +55,7 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         if (DO0) {
-            if (stash_row != nullptr) *reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col) = r0[i];
+            if (stash_row != nullptr) store_stream(reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col), r0[i]);
             E el[VEC];
             __builtin_memcpy(el, &r0[i], VB);
 #pragma unroll
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     if (!live && stash_row != nullptr) {
         V zero;
         __builtin_memset(&zero, 0, VB);
-        for (int n = 0; n < p.width0; ++n) *reinterpret_cast<V*>(stash_row + int64_t(n) * p.hd + col) = zero;
+        for (int n = 0; n < p.width0; ++n) store_stream(reinterpret_cast<V*>(stash_row + int64_t(n) * p.hd + col), zero);
     }
 
     const int wmax = TWO && p.width1 > p.width0 ? p.width1 : p.width0;
@@ -176,14 +176,15 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     if (p.out_vec && VEC % 4 == 0) {
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) {
-            *reinterpret_cast<float4*>(o0 + e) = make_float4(acc0[e], acc0[e + 1], acc0[e + 2], acc0[e + 3]);
-            if (TWO) *reinterpret_cast<float4*>(o1 + e) = make_float4(acc1[e], acc1[e + 1], acc1[e + 2], acc1[e + 3]);
+            store_stream(reinterpret_cast<float4*>(o0 + e), make_float4(acc0[e], acc0[e + 1], acc0[e + 2], acc0[e + 3]));
+            if (TWO)
+                store_stream(reinterpret_cast<float4*>(o1 + e), make_float4(acc1[e], acc1[e + 1], acc1[e + 2], acc1[e + 3]));
         }
     } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            o0[e] = acc0[e];
-            if (TWO) o1[e] = acc1[e];
+            store_stream(o0 + e, acc0[e]);
+            if (TWO) store_stream(o1 + e, acc1[e]);
         }
     }
 }

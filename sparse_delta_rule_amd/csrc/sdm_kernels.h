@@ -17,6 +17,27 @@ template <> struct RawVec<8> { using T = uint2; };
 template <> struct RawVec<4> { using T = uint32_t; };
 template <> struct RawVec<2> { using T = uint16_t; };
 
+// Stores of data the kernel writes once and never reads back (outputs, the
+// stash): marked non-temporal so the lines are not kept in the caches, which
+// leaves their capacity to the random row reads sharing the memory system.
+typedef uint32_t StreamU32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t StreamU32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+    const StreamU32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<StreamU32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(uint2* p, uint2 v) {
+    const StreamU32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<StreamU32x2*>(p));
+}
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(uint16_t* p, uint16_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+    store_stream(reinterpret_cast<uint4*>(p),
+                 make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float widen(float f) { return f; }
 
@@ -101,6 +122,11 @@ struct DecodeParams {
     int k_bytes, q_bytes, val_bytes;  // element sizes of k_idx, q_idx and the values
 };
 
+// Which decode kernel runs: one step, or the compact or wide multi-step loop.
+constexpr int kLoopSingle = 0;
+constexpr int kLoopCompact = 1;
+constexpr int kLoopWide = 2;
+
 struct DecodeGeometry {
     int vb;      // bytes per vector load: 16, 8, 4 or 2
     int vpr;     // vectors per row
@@ -109,10 +135,16 @@ struct DecodeGeometry {
     int rg;      // row groups: fixes the summation order
     int jn;      // rows per lane per phase: 1, 2, 4 or 8
     int threads; // lpr * rg
+    int loop;    // kLoopSingle, kLoopCompact or kLoopWide
     size_t lds;  // dynamic LDS bytes
 };
 
-DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, bool multi_step);
+// steps > 1 picks a multi-step loop: the wide one where the grid leaves at most
+// two waves on each SIMD of `cus` compute units (and a workgroup has at most
+// 256 threads), else the compact one. force_loop (kLoopCompact or kLoopWide,
+// or -1 for none) overrides that choice where the wide loop can run.
+DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_addr, int64_t steps,
+                               int64_t streams, int cus, int force_loop);
 hipError_t launch_decode(const DecodeParams& p, const DecodeGeometry& geo, bool bf16, hipStream_t stream);
 
 // ------------------------------------------------------------------ gather

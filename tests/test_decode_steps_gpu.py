@@ -4,7 +4,9 @@ One launch advances every stream by T tokens; the result must equal T
 single-step calls bit for bit, and the oracle stepped T times in the kernel's
 documented summation order. Cases stress the pipelining across tokens: rows a
 token writes that the next token reads or writes, and prefetch geometries with
-one and with several metadata items per thread.
+one and with several metadata items per thread. The library has two loops for
+this call (chosen by how many waves the grid puts on a SIMD); each case runs
+with the automatic choice and with each loop pinned through SDM_STEPS_LOOP.
 """
 
 import numpy as np
@@ -23,6 +25,17 @@ DEV = torch.device("cuda", 0)
 
 def _say(*a):
     print(*a, flush=True)
+
+
+@pytest.fixture(params=["auto", "compact", "wide"])
+def loop(request, monkeypatch):
+    """Pin the multi-step loop (the wide one runs only where a workgroup has at most
+    256 threads; elsewhere "wide" falls back to the compact loop)."""
+    if request.param == "auto":
+        monkeypatch.delenv("SDM_STEPS_LOOP", raising=False)
+    else:
+        monkeypatch.setenv("SDM_STEPS_LOOP", request.param)
+    return request.param
 
 
 def _sequence(wl, seed, device, steps):
@@ -61,7 +74,7 @@ def check_steps(wl: gen.DecodeWorkload, seed: int, streams_checked, *, steps=Non
     return bank, readings
 
 
-def test_config_c0_all_tokens():
+def test_config_c0_all_tokens(loop):
     wl = gen.WORKLOADS["c0"]
     for seed in (0, 1):
         check_steps(wl, seed, [0, 1, 2, 3])
@@ -82,17 +95,17 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_shapes(case):
+def test_shapes(case, loop):
     name, dt, S, P, hd, W, R, G, idt, vdt, T = case
     wl = gen.DecodeWorkload(name=name, bank_dtype=dt, streams=S, slots_per_stream=P, head_dim=hd, W=W, R=R,
                             G=G, steps=T, idx_dtype=idt, weights="normal_sqrtw", beta="sigmoid", g_low=-0.2,
                             bank_std=0.5, val_dtype=vdt)
-    _say("steps:", name)
+    _say("steps:", name, "loop:", loop)
     check_steps(wl, 3, list(range(S)))
 
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
-def test_every_token_rewrites_the_same_rows(dt):
+def test_every_token_rewrites_the_same_rows(dt, loop):
     """Each stream owns exactly W slots, written and read by every token: token t + 1's
     row loads must see token t's writes (the loads issued right after the barrier)."""
     W = 32
@@ -102,7 +115,7 @@ def test_every_token_rewrites_the_same_rows(dt):
     check_steps(wl, 5, list(range(24)))
 
 
-def test_reads_of_next_tokens_writes_are_not_early():
+def test_reads_of_next_tokens_writes_are_not_early(loop):
     """Token t reads exactly the slots token t + 1 writes: those reads must see token t's
     state (token t + 1's writes come later), while token t + 1's rows are already loading."""
     W = 16
@@ -131,7 +144,23 @@ def test_zero_tokens_and_errors():
                          torch.zeros(2, 1, 1, device=DEV), idx, val)
 
 
-def test_graph_replays_match_eager():
+def test_unknown_loop_name_is_rejected(monkeypatch):
+    from sparse_delta_rule_amd import SdmError
+    monkeypatch.setenv("SDM_STEPS_LOOP", "fastest")
+    bank = torch.zeros(64, 8, device=DEV)
+    idx = torch.zeros(2, 1, 2, dtype=torch.int64, device=DEV)
+    idx[:, :, 1] = 1
+    val = torch.zeros(2, 1, 2, device=DEV)
+    with pytest.raises(SdmError, match="SDM_STEPS_LOOP"):
+        sdm_decode_steps(bank, idx, val, torch.zeros(2, 1, 8, device=DEV), torch.zeros(2, 1, 1, device=DEV),
+                         torch.zeros(2, 1, 1, device=DEV), idx, val)
+    monkeypatch.setenv("SDM_STEPS_LOOP", "compact")
+    sdm_decode_steps(bank, idx, val, torch.zeros(2, 1, 8, device=DEV), torch.zeros(2, 1, 1, device=DEV),
+                     torch.zeros(2, 1, 1, device=DEV), idx, val)
+    torch.cuda.synchronize()
+
+
+def test_graph_replays_match_eager(loop):
     """The benchmark's launch path: sdm_decode_steps captured in a HIP graph. Every
     replay, with eager torch work and synchronisations between replays, must equal an
     eager launch from the same starting bank."""
@@ -158,13 +187,19 @@ def test_graph_replays_match_eager():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,checked", [
-    ("c1", [0, 333, 1023]),
-    ("c2", [0, 2047, 4095]),
-    ("c4", [0, 255, 511]),
+@pytest.mark.parametrize("name,checked,pin", [
+    ("c1", [0, 333, 1023], None),       # automatic choice: wide (two waves per SIMD)
+    ("c1", [0, 333, 1023], "compact"),
+    ("c2", [0, 2047, 4095], None),      # automatic choice: compact
+    ("c2", [0, 2047, 4095], "wide"),
+    ("c4", [0, 255, 511], None),        # 1024-thread workgroups: compact only
 ])
-def test_full_size_configs(name, checked):
+def test_full_size_configs(name, checked, pin, monkeypatch):
+    if pin is None:
+        monkeypatch.delenv("SDM_STEPS_LOOP", raising=False)
+    else:
+        monkeypatch.setenv("SDM_STEPS_LOOP", pin)
     wl = gen.WORKLOADS[name]
-    _say(f"steps {name}: {wl.name}")
+    _say(f"steps {name}: {wl.name}, loop {pin or 'auto'}")
     check_steps(wl, 0, checked, device=DEV, also_single=False)
     torch.cuda.empty_cache()
