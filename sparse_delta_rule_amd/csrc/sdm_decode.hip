@@ -209,10 +209,28 @@ __device__ __forceinline__ void row_partials(const typename RawVec<VB>::T (&row)
     for (int e = 0; e < VEC; ++e) partial[ln.grp * ln.slice_cols + ln.lane * VEC + e] = acc[e];
 }
 
-// Column col's total over the row groups, in group order from +0.
+// Column col's total over the row groups, in group order from +0. A chunk's LDS
+// reads are all issued before its first add, so the reads do not wait for one
+// another; the adds stay in group order.
 __device__ __forceinline__ float column_total(const float* partial, int rg, int slice_cols, int col) {
     float total = 0.0f;
-    for (int j = 0; j < rg; ++j) total += partial[j * slice_cols + col];
+    int j = 0;
+    for (; j + 8 <= rg; j += 8) {
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = partial[(j + k) * slice_cols + col];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) total += x[k];
+    }
+    if (j + 4 <= rg) {
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = partial[(j + k) * slice_cols + col];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) total += x[k];
+        j += 4;
+    }
+    for (; j < rg; ++j) total += partial[j * slice_cols + col];
     return total;
 }
 
@@ -223,32 +241,62 @@ __device__ __forceinline__ void form_delta(const DecodeParams& p, const Stage& s
         if (ln.col0 + col < p.hd) dv[col] = st.beta[0] * (st.v[col] - column_total(partial, p.rg, ln.slice_cols, col));
 }
 
+// Slot, k_val and decay of the W rows this lane holds (row w = grp + j RG; rows
+// past W repeat row W - 1 and are never written), read out of a Stage.
+template <int JN>
+struct Held {
+    int64_t slot[JN];
+    float kv[JN], d[JN];
+};
+
+template <int JN>
+__device__ __forceinline__ void hold_write_meta(Held<JN>& h, const Stage& st, int W, int rg, const Lane& ln) {
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+        const int w = ln.grp + j * rg, wc = w < W ? w : W - 1;
+        h.slot[j] = st.kslot[wc];
+        h.kv[j] = st.kv[wc];
+        h.d[j] = st.d[wc];
+    }
+}
+
+// Request the held rows, all before any is used.
+template <typename E, int VB, int JN>
+__device__ __forceinline__ void load_held_rows(typename RawVec<VB>::T (&row)[JN], const E* bank, const Held<JN>& h,
+                                               int64_t hd, const Lane& ln) {
+    using V = typename RawVec<VB>::T;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) row[j] = *reinterpret_cast<const V*>(bank + h.slot[j] * hd + ln.vcol);
+}
+
 // Decay-and-write of the W rows this lane holds. Write slots are distinct within
 // a stream, so plain stores suffice. opaque() hides the raw bits from the
 // optimiser, so the rows are widened again here instead of being kept widened
 // (twice the registers for bfloat16) across the barriers before this point.
 template <typename E, int VB, int JN>
-__device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E* bank, const Stage& st,
+__device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E* bank, const Held<JN>& h,
                                            const float* dv, int W, int rg, int64_t hd, const Lane& ln) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
 #pragma unroll
     for (int j = 0; j < JN; ++j) opaque(row[j]);
+    float dvl[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dvl[e] = dv[ln.lane * VEC + e];
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
         const int w = ln.grp + j * rg;
         if (ln.active && w < W) {
             E el[VEC], out[VEC];
             __builtin_memcpy(el, &row[j], VB);
-            const float kv = st.kv[w], d = st.d[w];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const float decayed = widen(el[e]) * d;
-                out[e] = narrow<E>(__builtin_fmaf(kv, dv[ln.lane * VEC + e], decayed));
+                const float decayed = widen(el[e]) * h.d[j];
+                out[e] = narrow<E>(__builtin_fmaf(h.kv[j], dvl[e], decayed));
             }
             V o;
             __builtin_memcpy(&o, out, VB);
-            *reinterpret_cast<V*>(bank + st.kslot[w] * hd + ln.vcol) = o;
+            *reinterpret_cast<V*>(bank + h.slot[j] * hd + ln.vcol) = o;
         }
     }
 }
@@ -299,7 +347,9 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
     __syncthreads();
     form_delta(p, st, partial, dv, ln);
     __syncthreads();
-    write_back<E, VB, JN>(row, bank, st, dv, p.W, p.rg, p.hd, ln);
+    Held<JN> h;
+    hold_write_meta(h, st, p.W, p.rg, ln);
+    write_back<E, VB, JN>(row, bank, h, dv, p.W, p.rg, p.hd, ln);
 
     // Ordering point: the write-back is visible to the loads below, for read slots
     // that are also write slots. No other workgroup touches these columns of
@@ -351,7 +401,9 @@ __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodePara
         __syncthreads();
         form_delta(p, st, partial, dv, ln);
         __syncthreads();
-        write_back<E, VB, JN>(wrow, bank, st, dv, p.W, p.rg, p.hd, ln);
+        Held<JN> h;
+        hold_write_meta(h, st, p.W, p.rg, ln);
+        write_back<E, VB, JN>(wrow, bank, h, dv, p.W, p.rg, p.hd, ln);
         // step t + 1's metadata (fetched during step t - 1) into the other buffer,
         // whose last reader (step t - 1's readings) finished before the barrier
         // that ended step t - 1.
@@ -374,14 +426,17 @@ __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodePara
 }
 
 // Wide loop, for grids that leave at most two waves on each SIMD, where the
-// memory parallelism has to come from within each wave: iteration t: request the R rows of step t and the W rows of step t + 1 (and
-// step t + 2's metadata) together; one pass forms both partial sums (separate
-// LDS buffers); barrier; readings of step t and delta_v of step t + 1; barrier;
-// write-back of step t + 1 and staging of step t + 2's metadata; barrier (the
-// ordering point for the next iteration's loads). Three barriers per step. Up to
-// 256 threads per workgroup, and the register budget of two waves per SIMD, so
-// the compiler keeps both row sets and the fetched metadata in flight at once
-// instead of trading that for occupancy the grid cannot use.
+// memory parallelism has to come from within each wave. Iteration t: request the
+// R rows of step t and the W rows of step t + 1 together, and while they are in
+// flight stage step t + 2's metadata (fetched during the previous iteration;
+// three Stage buffers rotate) and fetch step t + 3's; keep the slot, k_val and
+// decay of each held write row in registers; one pass forms both partial sums
+// (separate LDS buffers); barrier; readings of step t and delta_v of step
+// t + 1; barrier; write-back of step t + 1; barrier (the ordering point for the
+// next iteration's loads). Three barriers per step. At most 256 threads per
+// workgroup, and the register budget of two waves per SIMD, so the compiler
+// keeps both row sets and the fetched metadata in flight at once instead of
+// trading that for occupancy the grid cannot use.
 template <typename E, int VB, int JN, int MK, int MV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void sdm_decode_steps_wide_kernel(const DecodeParams p) {
@@ -390,34 +445,38 @@ void sdm_decode_steps_wide_kernel(const DecodeParams p) {
     extern __shared__ __align__(16) char s_raw[];
     const Lane ln = lane_geometry<VEC>(p);
     const int64_t s = blockIdx.x;
-    const size_t sb = stage_bytes(p.W, p.R, ln.slice_cols);  // two Stage buffers, alternating by step
-    float* wpart = reinterpret_cast<float*>(s_raw + 2 * sb);  // retrieval partials [RG][slice]
+    const size_t sb = stage_bytes(p.W, p.R, ln.slice_cols);  // three Stage buffers: step t in buffer t % 3
+    float* wpart = reinterpret_cast<float*>(s_raw + 3 * sb);  // retrieval partials [RG][slice]
     float* rpart = wpart + p.rg * ln.slice_cols;              // readings partials [RG][slice]
     float* dv = rpart + p.rg * ln.slice_cols;
     E* bank = static_cast<E*>(p.bank);
     const int T = p.steps;
 
-    // step 0's write, alone: stage, request rows, retrieval, delta_v, write-back,
-    // and step 1's metadata into the other buffer.
+    // step 0's write, alone: stage, request rows, retrieval, delta_v, write-back;
+    // step 1's metadata staged, step 2's fetched.
     const Stage st0 = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
     stage_direct<E>(p, 0, s, st0, ln.col0, ln.slice_cols);
     Meta<MK, MV> m;
     meta_load(p, min(1, T - 1), s, ln.col0, m);
     __syncthreads();
     V wrow[JN], rrow[JN];
-    load_rows<E, VB, JN>(wrow, bank, st0.kslot, p.W, p.rg, p.hd, ln);
+    Held<JN> h;
+    hold_write_meta(h, st0, p.W, p.rg, ln);
+    load_held_rows<E, VB, JN>(wrow, bank, h, p.hd, ln);
+    if (T > 1) meta_store<E, MK, MV>(p, m, carve_stage(s_raw + sb, p.W, p.R, ln.slice_cols), ln.col0,
+                                     ln.slice_cols);
+    meta_load(p, min(2, T - 1), s, ln.col0, m);
     row_partials<E, VB, JN>(wrow, st0.coef, p.W, p.rg, ln, wpart);
     __syncthreads();
     form_delta(p, st0, wpart, dv, ln);
     __syncthreads();
-    write_back<E, VB, JN>(wrow, bank, st0, dv, p.W, p.rg, p.hd, ln);
-    if (T > 1) meta_store<E, MK, MV>(p, m, carve_stage(s_raw + sb, p.W, p.R, ln.slice_cols), ln.col0,
-                                     ln.slice_cols);
+    write_back<E, VB, JN>(wrow, bank, h, dv, p.W, p.rg, p.hd, ln);
     __syncthreads();
 
+    int b0 = 0, b1 = 1, b2 = 2;  // buffers of steps t, t + 1, t + 2
     for (int t = 0; t < T; ++t) {
-        const Stage st = carve_stage(s_raw + (t & 1) * sb, p.W, p.R, ln.slice_cols);
-        const Stage nx = carve_stage(s_raw + ((t + 1) & 1) * sb, p.W, p.R, ln.slice_cols);
+        const Stage st = carve_stage(s_raw + b0 * sb, p.W, p.R, ln.slice_cols);
+        const Stage nx = carve_stage(s_raw + b1 * sb, p.W, p.R, ln.slice_cols);
         const bool more = t + 1 < T;
         // Step t's writes are visible here (the barrier above); both row sets may
         // contain slots step t wrote. The load phase has no branch (a guarded load
@@ -426,24 +485,29 @@ void sdm_decode_steps_wide_kernel(const DecodeParams p) {
         // go unused.
         const Stage& ws = more ? nx : st;
         load_rows<E, VB, JN>(rrow, bank, st.qslot, p.R, p.rg, p.hd, ln);
-        load_rows<E, VB, JN>(wrow, bank, ws.kslot, p.W, p.rg, p.hd, ln);
-        meta_load(p, min(t + 2, T - 1), s, ln.col0, m);
+        hold_write_meta(h, ws, p.W, p.rg, ln);
+        load_held_rows<E, VB, JN>(wrow, bank, h, p.hd, ln);
+        // Step t + 2's buffer last held step t - 1, whose readers all finished
+        // before the barrier that ended the previous iteration; its new contents
+        // are read after this iteration's barriers.
+        if (t + 2 < T)
+            meta_store<E, MK, MV>(p, m, carve_stage(s_raw + b2 * sb, p.W, p.R, ln.slice_cols), ln.col0,
+                                  ln.slice_cols);
+        meta_load(p, min(t + 3, T - 1), s, ln.col0, m);
         row_partials<E, VB, JN>(rrow, st.qv, p.R, p.rg, ln, rpart);
         row_partials<E, VB, JN>(wrow, ws.coef, p.W, p.rg, ln, wpart);
         __syncthreads();
         store_readings<E>(p, rpart, int64_t(t) * p.streams + s, ln);
         if (more) form_delta(p, nx, wpart, dv, ln);
         __syncthreads();
-        if (more) {
-            write_back<E, VB, JN>(wrow, bank, nx, dv, p.W, p.rg, p.hd, ln);
-            // step t + 2's metadata into this step's buffer, whose last readers (the
-            // loads and partials of step t's reads) finished before the first barrier
-            // of this iteration.
-            if (t + 2 < T) meta_store<E, MK, MV>(p, m, st, ln.col0, ln.slice_cols);
-        }
+        if (more) write_back<E, VB, JN>(wrow, bank, h, dv, p.W, p.rg, p.hd, ln);
         // Ordering point: step t + 1's write-back is visible to the next iteration's
-        // loads, and step t + 2's metadata is staged.
+        // loads.
         __syncthreads();
+        const int b = b0;
+        b0 = b1;
+        b1 = b2;
+        b2 = b;
     }
 }
 
@@ -524,9 +588,9 @@ DecodeGeometry decode_geometry(int es, int64_t hd, int W, int R, uintptr_t bank_
     const bool wide_fits = g.threads <= 256;
     g.loop = wide_fits && waves_per_simd <= 2 ? kLoopWide : kLoopCompact;
     if (force_loop == kLoopCompact || (force_loop == kLoopWide && wide_fits)) g.loop = force_loop;
-    // two staging buffers, then one partial buffer (compact) or two (wide), and
-    // delta_v
-    g.lds = 2 * stage + cols * size_t((g.loop == kLoopWide ? 2 : 1) * g.rg + 1);
+    // two staging buffers and one partial buffer (compact), or three staging
+    // buffers and two partial buffers (wide); then delta_v
+    g.lds = g.loop == kLoopWide ? 3 * stage + cols * size_t(2 * g.rg + 1) : 2 * stage + cols * size_t(g.rg + 1);
     return g;
 }
 
