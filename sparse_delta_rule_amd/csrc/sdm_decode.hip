@@ -287,16 +287,15 @@ __device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E*
     for (int j = 0; j < JN; ++j) {
         const int w = ln.grp + j * rg;
         if (ln.active && w < W) {
-            E el[VEC], out[VEC];
+            E el[VEC];
+            float out[VEC];
             __builtin_memcpy(el, &row[j], VB);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const float decayed = widen(el[e]) * h.d[j];
-                out[e] = narrow<E>(__builtin_fmaf(h.kv[j], dvl[e], decayed));
+                out[e] = __builtin_fmaf(h.kv[j], dvl[e], decayed);
             }
-            V o;
-            __builtin_memcpy(&o, out, VB);
-            *reinterpret_cast<V*>(bank + h.slot[j] * hd + ln.vcol) = o;
+            *reinterpret_cast<V*>(bank + h.slot[j] * hd + ln.vcol) = Pack<E, VB>::of(out);
         }
     }
 }

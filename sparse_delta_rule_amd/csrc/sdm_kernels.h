@@ -41,16 +41,22 @@ __device__ __forceinline__ void store_stream(float4* p, float4 v) {
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float widen(float f) { return f; }
 
-// float32 -> bfloat16 bits, round to nearest even: adding 0x7fff plus the kept
-// half's lowest bit carries into the kept half exactly when the dropped half is
-// above one half, or equal to it with an odd kept half. NaN stays a quiet NaN.
-// Branch-free (a select), so a wavefront never diverges on it.
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t quiet_nan = (u >> 16) | 0x40u;
-    return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);
+// float32 -> bfloat16 bits, round to nearest even, NaN kept a NaN with its quiet
+// bit set: gfx950's packed conversion (two values per instruction). Its result
+// equals the bit-level definition (add 0x7fff plus the kept half's lowest bit,
+// keep the high half; for a NaN, the high half with the quiet bit set) for every
+// one of the 2^32 float32 inputs, denormals included, at this library's default
+// floating-point mode.
+typedef __bf16 Bf16x2 __attribute__((ext_vector_type(2)));
+typedef float F32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t to_bf16x2_rne(float lo, float hi) {
+    const F32x2 f = {lo, hi};
+    const Bf16x2 h = __builtin_convertvector(f, Bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
 }
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) { return uint16_t(to_bf16x2_rne(f, 0.0f)); }
 
 // Make a register's contents opaque to the optimiser (no instruction is
 // emitted): values derived from it before this point are not reused after it.
@@ -68,6 +74,30 @@ __device__ __forceinline__ void opaque(uint16_t& v) {
 template <typename E> __device__ __forceinline__ E narrow(float f);
 template <> __device__ __forceinline__ uint16_t narrow<uint16_t>(float f) { return to_bf16_rne(f); }
 template <> __device__ __forceinline__ float narrow<float>(float f) { return f; }
+
+// VEC float32 results as one vector of bank elements (pairs converted together).
+template <typename E, int VB> struct Pack;
+template <int VB> struct Pack<float, VB> {
+    static __device__ __forceinline__ typename RawVec<VB>::T of(const float (&r)[VB / 4]) {
+        typename RawVec<VB>::T o;
+        __builtin_memcpy(&o, r, VB);
+        return o;
+    }
+};
+template <int VB> struct Pack<uint16_t, VB> {
+    static __device__ __forceinline__ typename RawVec<VB>::T of(const float (&r)[VB / 2]) {
+        typename RawVec<VB>::T o;
+        if constexpr (VB == 2) {
+            o = to_bf16_rne(r[0]);
+        } else {
+            uint32_t w[VB / 4];
+#pragma unroll
+            for (int i = 0; i < VB / 4; ++i) w[i] = to_bf16x2_rne(r[2 * i], r[2 * i + 1]);
+            __builtin_memcpy(&o, w, VB);
+        }
+        return o;
+    }
+};
 
 // Round a float32 to the bank element type and widen it back.
 template <typename E> __device__ __forceinline__ float to_bank(float f) { return widen(narrow<E>(f)); }

@@ -1,0 +1,87 @@
+"""Rounding to a bfloat16 bank at exact ties, on the GPU against the oracle.
+
+Random inputs almost never land exactly halfway between two bfloat16 values,
+so these inputs are built to: bank rows and v on the bfloat16 grid in [1, 2),
+k_val = 1, g = 0 (decay 1) and beta = 1/2 make every written value
+row + (v - row) / 2, an exact tie whenever the two mantissas differ by an odd
+count (about half of all elements). The value read back is q_val times a
+written row, a product that ties for some mantissa pairs, and q_val arrives in
+float32 with low halves 0x8000 (a tie), 0x7fff, 0x8001 and 0xffff, so its
+rounding to the bank dtype on the way in sees ties as well. The rounding is
+the one the pages fix for the bank (round to nearest, ties to even); the
+oracle implements it bit by bit, and the comparison is bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_delta_rule_amd import sdm_decode_step, sdm_decode_steps
+from tests.helpers import bits_equal, step_to_numpy, to_np_bank
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+S, P, HD = 512, 4, 64
+
+
+def _grid(gen, shape):
+    """bfloat16-exact values 1 + m / 128, m in 0..127."""
+    return 1.0 + torch.randint(0, 128, shape, generator=gen).float() / 128.0
+
+
+def _inputs(gen, read_written: bool):
+    k_idx = (torch.arange(S, dtype=torch.int64) * P).view(S, 1)
+    q_idx = k_idx if read_written else k_idx + 1 + torch.randint(0, P - 1, (S, 1), generator=gen)
+    hi = (_grid(gen, (S, 1)).view(torch.int32) >> 16) << 16
+    lo = torch.tensor([0x0000, 0x8000, 0x7FFF, 0x8001, 0xFFFF], dtype=torch.int32)
+    q_val = (hi | lo[torch.randint(0, 5, (S, 1), generator=gen)]).view(torch.float32)
+    return {"k_idx": k_idx, "k_val": torch.ones(S, 1), "v": _grid(gen, (S, HD)), "beta": torch.full((S, 1), 0.5),
+            "g": torch.zeros(S, 1), "q_idx": q_idx, "q_val": q_val}
+
+
+def _ties_in_writes(bank_rows: np.ndarray, v: np.ndarray) -> int:
+    """Written values row + (v - row) / 2 that lie exactly halfway between bfloat16 values."""
+    row = (bank_rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    val = (row + (v.astype(np.float64) - row) / 2).astype(np.float32)  # exact: 9 significant bits
+    return int(np.count_nonzero((val.view(np.uint32) & 0xFFFF) == 0x8000))
+
+
+@pytest.fixture(params=["auto", "compact", "wide"])
+def loop(request, monkeypatch):
+    if request.param == "auto":
+        monkeypatch.delenv("SDM_STEPS_LOOP", raising=False)
+    else:
+        monkeypatch.setenv("SDM_STEPS_LOOP", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("read_written", [True, False], ids=["read-written", "read-other"])
+def test_single_step_ties(read_written):
+    gen = torch.Generator().manual_seed(17)
+    bank = _grid(gen, (S * P, HD)).to(torch.bfloat16)
+    ref_bank = to_np_bank(bank)
+    inp = _inputs(gen, read_written)
+    npin = step_to_numpy(inp)
+    ties = _ties_in_writes(ref_bank[npin["k_idx"].ravel()], npin["v"])
+    assert ties > 0.3 * S * HD, f"only {ties} ties among the written values"
+    bank = bank.to(DEV)
+    readings = sdm_decode_step(bank, **{k: t.to(DEV) for k, t in inp.items()})
+    ref = oracle.decode_step(ref_bank, **npin, groups=1)
+    assert bits_equal(to_np_bank(readings), ref), "readings differ from the oracle"
+    assert bits_equal(to_np_bank(bank), ref_bank), "bank differs from the oracle"
+
+
+def test_multi_step_ties(loop):
+    gen = torch.Generator().manual_seed(23)
+    T = 4
+    bank = _grid(gen, (S * P, HD)).to(torch.bfloat16)
+    ref_bank = to_np_bank(bank)
+    per = [_inputs(gen, t % 2 == 0) for t in range(T)]
+    seq = {k: torch.stack([p[k] for p in per]) for k in per[0]}
+    bank = bank.to(DEV)
+    readings = sdm_decode_steps(bank, **{k: t.to(DEV) for k, t in seq.items()})
+    for t in range(T):
+        ref = oracle.decode_step(ref_bank, **step_to_numpy(per[t]), groups=1)
+        assert bits_equal(to_np_bank(readings[t]), ref), f"token {t}: readings differ from the oracle"
+    assert bits_equal(to_np_bank(bank), ref_bank), "bank differs from the oracle"
