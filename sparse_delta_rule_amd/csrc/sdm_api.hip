@@ -386,7 +386,7 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
     }
 
     const sdm::GatherGeometry geo = sdm::gather_geometry(es, head_dim, reinterpret_cast<uintptr_t>(bank),
-                                                         reinterpret_cast<uintptr_t>(stash));
+                                                         reinterpret_cast<uintptr_t>(stash), two);
     const int64_t blocks = (tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
     if (blocks > 0x7fffffffLL || geo.slices > 65535)
         return fail(SDM_E_SHAPE, "sdm_gather: %lld tokens x %d column slices exceed the grid", (long long)tokens,

@@ -191,7 +191,7 @@ struct GatherParams {
     int64_t hd, tokens, chunk, valid;
     int width0, width1;
     int vpr;  // vectors per row
-    int lpr;  // lanes per token: a power of two <= 64
+    int lpr;  // lanes per (token, operand) pair: a power of two <= 64
     int idx64, w_bf16;
     int out_vec;  // outputs aligned for whole-vector float stores
 };
@@ -205,7 +205,7 @@ struct GatherGeometry {
     int threads;
 };
 
-GatherGeometry gather_geometry(int es, int64_t hd, uintptr_t bank_addr, uintptr_t stash_addr);
+GatherGeometry gather_geometry(int es, int64_t hd, uintptr_t bank_addr, uintptr_t stash_addr, bool two);
 hipError_t launch_gather(const GatherParams& p, const GatherGeometry& geo, bool bf16, bool two,
                          hipStream_t stream);
 
