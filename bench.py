@@ -25,6 +25,7 @@ import argparse
 import glob
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -45,18 +46,28 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(config: str, kernel: str):
-    """HBM bytes per launch measured by rocprofv3 counters for this config and kernel,
-    if they were taken on the current kernel sources (profiles/traffic.json), else None."""
+def launch_kind(config: str, entry: str) -> str:
+    """What one timed launch runs: the gather, the multi-token decode or the single step."""
+    return "gather" if config == "c3" else ("steps" if entry == "steps" else "step")
+
+
+# Name fragment that selects a launch kind's kernels in a rocprofv3 trace (the
+# multi-token decode has two loops; the library picks one per launch shape).
+KERNEL_PATTERN = {"gather": "sdm_gather_kernel", "steps": "sdm_decode_steps", "step": "sdm_decode_kernel"}
+
+
+def stored_traffic(config: str, kind: str):
+    """(HBM bytes per launch, kernel name) measured by rocprofv3 for this config and launch
+    kind, if taken on the current kernel sources (profiles/traffic.json), else (None, None)."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         data = json.load(f)
-    entry = data.get(f"{config}/{kernel}")
+    entry = data.get(f"{config}/{kind}")
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return entry.get("bytes_per_launch")
+        return None, None
+    return entry.get("bytes_per_launch"), entry.get("kernel")
 
 
 def parse_args(argv=None):
@@ -204,7 +215,6 @@ def bench_decode(torch, args, cfg_name, wl):
             sdm_decode_steps(bank, **stacked, readings=readings)
 
         launches, per_launch = K // T, T
-        kernel = "sdm_decode_steps_kernel"
     else:
         readings = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
 
@@ -213,7 +223,6 @@ def bench_decode(torch, args, cfg_name, wl):
             sdm_decode_step(bank, **seq[j], readings=readings[j])
 
         launches, per_launch = K, 1
-        kernel = "sdm_decode_kernel"
     ms = _run_steps(torch, args, launch_one, launches)
     ms_step = ms / K
     launch_bytes = row_bytes_step * per_launch
@@ -226,7 +235,7 @@ def bench_decode(torch, args, cfg_name, wl):
               "tokens_per_launch": per_launch, "launch": args.launch, "seed": args.seed}
     value = wl.streams * K / (ms * 1e-3)
     return dict(value=value, unit="stream-steps/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=launch_bytes, kernel=kernel, cpu=cpu, tokens_per_s=value)
+                row_bytes=launch_bytes, cpu=cpu, tokens_per_s=value)
 
 
 def bench_gather(torch, args, cfg_name, wl):
@@ -261,7 +270,7 @@ def bench_gather(torch, args, cfg_name, wl):
               "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "launch": args.launch, "seed": args.seed}
     value = T * K / (ms * 1e-3)
     return dict(value=value, unit="tokens/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=row_bytes, kernel="sdm_gather_kernel", cpu=cpu, tokens_per_s=value)
+                row_bytes=row_bytes, cpu=cpu, tokens_per_s=value)
 
 
 def calibrate_copy(torch):
@@ -317,11 +326,15 @@ def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
 
 def ingest_profile(args) -> int:
     trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
-    kernel = "sdm_gather_kernel" if args.config == "c3" else (
-        "sdm_decode_steps_kernel" if args.entry == "steps" else "sdm_decode_kernel")
-    stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if kernel in r["Name"]]
+    kind = launch_kind(args.config, args.entry)
+    pattern = KERNEL_PATTERN[kind]
+    stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if pattern in r["Name"]]
     if not stats:
-        raise SystemExit(f"bench.py: {kernel} not in the kernel trace under {trace}")
+        raise SystemExit(f"bench.py: no {pattern} kernel in the trace under {trace}")
+    names = {re.search(r"(sdm_\w+_kernel)", r["Name"]).group(1) for r in stats}
+    if len(names) != 1:
+        raise SystemExit(f"bench.py: several kernels ({sorted(names)}) in one launch kind's trace")
+    kernel = names.pop()
     calls = sum(int(r["Calls"]) for r in stats)
     avg_ns = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in stats) / calls
     f_kib, f_n = _counter_kib(fetch, kernel)
@@ -337,10 +350,10 @@ def ingest_profile(args) -> int:
     if os.path.exists(traffic_path):
         with open(traffic_path) as f:
             data = json.load(f)
-    data[f"{args.config}/{kernel}"] = {
+    data[f"{args.config}/{kind}"] = {
         "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fetch_b + write_b,
         "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
-        "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls}
+        "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls, "kernel": kernel}
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -392,7 +405,8 @@ def main(argv=None):
         r = bench_decode(torch, args, args.config, wl)
     else:
         r = bench_gather(torch, args, args.config, wl)
-    traffic = stored_traffic(args.config, r["kernel"])
+    kind = launch_kind(args.config, args.entry)
+    traffic, kernel = stored_traffic(args.config, kind)
     out = {
         "metric": METRIC,
         "value": r["value"],
@@ -409,7 +423,7 @@ def main(argv=None):
         "config": r["config"],
         "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": r["kernel"], "algorithmic_bytes_per_launch": r["row_bytes"]},
+                     "kernel": kernel or KERNEL_PATTERN[kind], "algorithmic_bytes_per_launch": r["row_bytes"]},
         "cpu_baseline": r["cpu"],
         "tokens_per_s": r["tokens_per_s"],
         "row_gbps": r["gbps"],

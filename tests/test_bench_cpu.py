@@ -1,0 +1,83 @@
+"""Host logic of bench.py that needs no GPU: the one-GPU guard, and turning
+rocprofv3 output (kernel trace and byte counters) into the stored HBM-traffic
+figures the benchmark line reports."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+WIDE = "void sdm::(anonymous namespace)::sdm_decode_steps_wide_kernel<unsigned short, 16, 4, 1, 1>(sdm::DecodeParams)"
+COMPACT = "void sdm::(anonymous namespace)::sdm_decode_steps_kernel<unsigned short, 16, 4, 1, 1>(sdm::DecodeParams)"
+COPY = "void at::native::elementwise_kernel<128, 4>(int, float)"
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _trace(d, kernels):
+    _write_csv(os.path.join(d, "run_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"],
+               [[k, calls, avg, avg - 1, avg + 1] for k, calls, avg in kernels])
+
+
+def _counter(d, rows):
+    _write_csv(os.path.join(d, "run_counter_collection.csv"), ["Kernel_Name", "Counter_Value"], rows)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_launch_kinds():
+    assert bench.launch_kind("c3", "steps") == "gather"
+    assert bench.launch_kind("c1", "steps") == "steps"
+    assert bench.launch_kind("c2", "step") == "step"
+
+
+def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    _trace(t, [(WIDE, 10, 300000.0), (COPY, 3, 5000.0)])
+    # FETCH_SIZE counts half the bytes on this part (a 1 GiB copy reads 524288 KiB): scale 2
+    _counter(f, [(WIDE, 500000.0), (WIDE, 500000.0), (COPY, 10.0)])
+    _counter(w, [(WIDE, 400000.0), (WIDE, 400000.0)])
+    _counter(cf, [(COPY, 524288.0), (COPY, 1.0)])
+    _counter(cw, [(COPY, 1048576.0)])
+    assert bench.main(["--config", "c1", "--ingest-profile", t, f, w, cf, cw, "--profile-commands", "cmds"]) == 0
+    with open(tmp_path / "profiles" / "traffic.json") as fh:
+        data = json.load(fh)
+    e = data["c1/steps"]
+    assert e["kernel"] == "sdm_decode_steps_wide_kernel"
+    assert e["fetch_scale"] == pytest.approx(2.0) and e["write_scale"] == pytest.approx(1.0)
+    assert e["bytes_per_launch"] == pytest.approx((500000.0 * 2 + 400000.0) * 1024)
+    assert e["avg_kernel_ns"] == pytest.approx(300000.0)
+    alg, _ = bench.algorithmic_bytes("c1", "steps")
+    assert e["algorithmic_bytes_per_launch"] == alg == 64 * 1024 * 96 * 256
+    assert (tmp_path / "profiles" / "sdm_decode_steps_wide_kernel_c1.md").exists()
+    # the stored figures apply while the kernel sources are unchanged
+    assert bench.stored_traffic("c1", "steps") == (e["bytes_per_launch"], "sdm_decode_steps_wide_kernel")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.stored_traffic("c1", "steps") == (None, None)
+
+
+def test_ingest_rejects_a_trace_with_both_decode_loops(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t = str(tmp_path / "trace")
+    _trace(t, [(WIDE, 5, 300000.0), (COMPACT, 5, 310000.0)])
+    with pytest.raises(SystemExit, match="several kernels"):
+        bench.main(["--config", "c1", "--ingest-profile", t, t, t, t, t])
