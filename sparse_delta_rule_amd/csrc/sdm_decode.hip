@@ -242,11 +242,25 @@ __device__ __forceinline__ void form_delta(const DecodeParams& p, const Stage& s
 }
 
 // Slot, k_val and decay of the W rows this lane holds (row w = grp + j RG; rows
-// past W repeat row W - 1 and are never written), read out of a Stage.
+// past W repeat row W - 1 and are never written), read out of a Stage into
+// registers ahead of time (the wide loop does this while its row loads are in
+// flight).
 template <int JN>
 struct Held {
     int64_t slot[JN];
     float kv[JN], d[JN];
+    __device__ __forceinline__ int64_t slot_of(int j, int) const { return slot[j]; }
+    __device__ __forceinline__ float kv_of(int j, int) const { return kv[j]; }
+    __device__ __forceinline__ float d_of(int j, int) const { return d[j]; }
+};
+
+// The same three values read from the Stage in LDS at the point of use (fewer
+// live registers, for the kernels that run at high occupancy).
+struct Staged {
+    const Stage* st;
+    __device__ __forceinline__ int64_t slot_of(int, int w) const { return st->kslot[w]; }
+    __device__ __forceinline__ float kv_of(int, int w) const { return st->kv[w]; }
+    __device__ __forceinline__ float d_of(int, int w) const { return st->d[w]; }
 };
 
 template <int JN>
@@ -273,8 +287,8 @@ __device__ __forceinline__ void load_held_rows(typename RawVec<VB>::T (&row)[JN]
 // a stream, so plain stores suffice. opaque() hides the raw bits from the
 // optimiser, so the rows are widened again here instead of being kept widened
 // (twice the registers for bfloat16) across the barriers before this point.
-template <typename E, int VB, int JN>
-__device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E* bank, const Held<JN>& h,
+template <typename E, int VB, int JN, typename RowMeta>
+__device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E* bank, const RowMeta& h,
                                            const float* dv, int W, int rg, int64_t hd, const Lane& ln) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
@@ -292,10 +306,10 @@ __device__ __forceinline__ void write_back(typename RawVec<VB>::T (&row)[JN], E*
             __builtin_memcpy(el, &row[j], VB);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const float decayed = widen(el[e]) * h.d[j];
-                out[e] = __builtin_fmaf(h.kv[j], dvl[e], decayed);
+                const float decayed = widen(el[e]) * h.d_of(j, w);
+                out[e] = __builtin_fmaf(h.kv_of(j, w), dvl[e], decayed);
             }
-            *reinterpret_cast<V*>(bank + h.slot[j] * hd + ln.vcol) = Pack<E, VB>::of(out);
+            *reinterpret_cast<V*>(bank + h.slot_of(j, w) * hd + ln.vcol) = Pack<E, VB>::of(out);
         }
     }
 }
@@ -346,9 +360,7 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
     __syncthreads();
     form_delta(p, st, partial, dv, ln);
     __syncthreads();
-    Held<JN> h;
-    hold_write_meta(h, st, p.W, p.rg, ln);
-    write_back<E, VB, JN>(row, bank, h, dv, p.W, p.rg, p.hd, ln);
+    write_back<E, VB, JN>(row, bank, Staged{&st}, dv, p.W, p.rg, p.hd, ln);
 
     // Ordering point: the write-back is visible to the loads below, for read slots
     // that are also write slots. No other workgroup touches these columns of
@@ -400,9 +412,7 @@ __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodePara
         __syncthreads();
         form_delta(p, st, partial, dv, ln);
         __syncthreads();
-        Held<JN> h;
-        hold_write_meta(h, st, p.W, p.rg, ln);
-        write_back<E, VB, JN>(wrow, bank, h, dv, p.W, p.rg, p.hd, ln);
+        write_back<E, VB, JN>(wrow, bank, Staged{&st}, dv, p.W, p.rg, p.hd, ln);
         // step t + 1's metadata (fetched during step t - 1) into the other buffer,
         // whose last reader (step t - 1's readings) finished before the barrier
         // that ended step t - 1.
