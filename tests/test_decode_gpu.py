@@ -159,6 +159,30 @@ def test_reads_see_this_steps_writes(dt):
     assert not torch.equal(readings, old)
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_reads_of_written_slots_permuted_and_repeated(dt):
+    """Reads drawn from this step's write slots (permuted, some repeated, mixed with
+    unwritten slots): against the oracle bit for bit."""
+    wl = gen.WORKLOADS["c1"].replace(streams=48, slots_per_stream=256, bank_dtype=dt)
+    bank = gen.decode_bank(wl, 12).to(DEV)
+    inp = {k: v.to(DEV) for k, v in gen.decode_step_inputs(wl, 12, 0).items()}
+    g = torch.Generator().manual_seed(13)
+    for s in range(wl.streams):
+        perm = torch.randperm(wl.W, generator=g)
+        take = torch.randint(0, 3, (wl.R,), generator=g)  # 0: a written slot, 1: repeat, 2: keep
+        q = inp["q_idx"][s].clone()
+        k = inp["k_idx"][s]
+        q[take == 0] = k[perm.to(DEV)][take == 0]
+        q[take == 1] = k[0]
+        inp["q_idx"][s] = q
+    npin = step_to_numpy(inp)
+    ref_bank = to_np_bank(bank)
+    ref = oracle.decode_step(ref_bank, **npin, groups=documented_decode_groups(wl.W, wl.R))
+    readings = sdm_decode_step(bank, **inp)
+    assert bits_equal(to_np_bank(readings), ref)
+    assert bits_equal(to_np_bank(bank), ref_bank)
+
+
 def test_heavy_read_write_overlap_c4_shape():
     """Config c4's shape (fp32, hd 100, W = R = 256 of 2048 slots: ~32 read slots per stream
     coincide with written ones) with q drawn from the written slots for half the streams."""
