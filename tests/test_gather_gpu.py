@@ -64,6 +64,7 @@ CASES = [
     ("hd256 bf16 32 lanes", torch.bfloat16, 1000, 256, 40, 20, 20, 256, torch.int32, torch.bfloat16),
     ("hd600 bf16 two slices", torch.bfloat16, 500, 600, 16, 8, 9, 4, torch.int32, torch.float32),
     ("hd1000 f32 four slices", torch.float32, 200, 1000, 8, 4, 5, 3, torch.int64, torch.float32),
+    ("hd128 bf16 widths 255/97", torch.bfloat16, 4000, 128, 40, 8, 255, 97, torch.int32, torch.bfloat16),
 ]
 
 
