@@ -22,7 +22,8 @@
 // its row loads. Entries are taken 32 at a time (fewer round trips per pair:
 // measured faster than 8 or 16 at the same bytes in flight per SIMD, although
 // it leaves two waves per SIMD), all of a batch's row loads issued before the
-// first is used. Padding tokens load no row.
+// first is used. Padding tokens load no row. Rows are loaded and outputs and
+// stash rows stored non-temporally: all of them are touched once.
 
 #include "sdm_kernels.h"
 
@@ -48,7 +49,7 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     float x[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        r[i] = *reinterpret_cast<const V*>(bank + int64_t(s_idx[k0 + i]) * hd + col);
+        r[i] = load_stream(reinterpret_cast<const V*>(bank + int64_t(s_idx[k0 + i]) * hd + col));
         x[i] = value_of<WT>(s_w[k0 + i]);
     }
 #pragma unroll

@@ -38,6 +38,19 @@ __device__ __forceinline__ void store_stream(float4* p, float4 v) {
                  make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
 }
 
+// Loads of rows read once and not written (the gather's): non-temporal, so they
+// do not displace lines the caches can still use.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    const StreamU32x4 w = __builtin_nontemporal_load(reinterpret_cast<const StreamU32x4*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+    const StreamU32x2 w = __builtin_nontemporal_load(reinterpret_cast<const StreamU32x2*>(p));
+    return make_uint2(w.x, w.y);
+}
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint16_t load_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ float widen(float f) { return f; }
 
