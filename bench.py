@@ -88,6 +88,9 @@ def parse_args(argv=None):
     p.add_argument("--ingest-profile", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="summarise rocprofv3 output directories of this config into profiles/ (no GPU)")
     p.add_argument("--profile-commands", default="", help="text of the commands that made the directories")
+    p.add_argument("--extra-counters", nargs="*", default=[], metavar="DIR",
+                   help="with --ingest-profile: rocprofv3 --pmc runs of TCC_HIT_sum/TCC_MISS_sum, VmemLatency, "
+                        "TCC_EA0_RDREQ_LEVEL_sum/TCC_EA0_RDREQ_sum, summarised as L2 hit rate and latencies")
     return p.parse_args(argv)
 
 
@@ -307,6 +310,29 @@ def _counter_kib(directory: str, name_part: str, min_kib: float = 0.0):
     return statistics.median(vals), len(vals)
 
 
+def _counters(directory: str, name_part: str) -> dict:
+    """Median per-dispatch value of every counter of a rocprofv3 --pmc run, over the
+    dispatches of the kernels whose name contains name_part."""
+    import statistics
+    vals = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if name_part in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def derived_counters(c: dict) -> dict:
+    """L2 hit rate and latencies from raw counter medians (those present)."""
+    out = {}
+    if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c and c["TCC_HIT_sum"] + c["TCC_MISS_sum"] > 0:
+        out["l2_hit_rate"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+    if "VmemLatency" in c:
+        out["vmem_latency_cycles"] = c["VmemLatency"]
+    if c.get("TCC_EA0_RDREQ_sum", 0) > 0 and "TCC_EA0_RDREQ_LEVEL_sum" in c:
+        out["ea_read_latency_cycles"] = c["TCC_EA0_RDREQ_LEVEL_sum"] / c["TCC_EA0_RDREQ_sum"]
+    return out
+
+
 def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
     """(bytes per launch, unit description) of the row traffic the method needs."""
     import gen
@@ -345,6 +371,10 @@ def ingest_profile(args) -> int:
     f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
     alg, alg_desc = algorithmic_bytes(args.config, args.entry)
+    raw = {}
+    for d in args.extra_counters:
+        raw.update(_counters(d, kernel))
+    derived = derived_counters(raw)
     traffic_path = os.path.join(PROFILES, "traffic.json")
     data = {}
     if os.path.exists(traffic_path):
@@ -353,7 +383,8 @@ def ingest_profile(args) -> int:
     data[f"{args.config}/{kind}"] = {
         "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fetch_b + write_b,
         "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
-        "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls, "kernel": kernel}
+        "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls, "kernel": kernel,
+        "counters": raw, **derived}
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -375,6 +406,20 @@ def ingest_profile(args) -> int:
         f.write(f"\nMeasured HBM traffic {(fetch_b + write_b) / 2**20:.1f} MiB per launch against "
                 f"{alg / 2**20:.1f} MiB of algorithmic row bytes (ratio {(fetch_b + write_b) / alg:.3f}; "
                 "the excess is slots, weights, values and outputs).\n")
+        if raw:
+            f.write("\n## Cache and latency counters (one `--pmc` pass per group)\n\n| counter | median per dispatch |\n|---|---|\n")
+            for k in sorted(raw):
+                f.write(f"| {k} | {raw[k]:.6g} |\n")
+            f.write("\n")
+            if "l2_hit_rate" in derived:
+                f.write(f"L2 hit rate TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) = {derived['l2_hit_rate']:.3f}. ")
+            if "vmem_latency_cycles" in derived:
+                f.write(f"Average VMEM instruction latency (VmemLatency: accumulated SQ_INST_LEVEL_VMEM / "
+                        f"SQ_INSTS_VMEM) = {derived['vmem_latency_cycles']:.0f} cycles. ")
+            if "ea_read_latency_cycles" in derived:
+                f.write(f"Average L2-to-memory read latency TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum = "
+                        f"{derived['ea_read_latency_cycles']:.0f} cycles.")
+            f.write("\n")
     print(json.dumps({"wrote": [traffic_path, md], "avg_kernel_us": avg_ns / 1e3,
                       "traffic_MiB": (fetch_b + write_b) / 2**20, "alg_MiB": alg / 2**20}))
     return 0

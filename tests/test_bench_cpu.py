@@ -81,3 +81,28 @@ def test_ingest_rejects_a_trace_with_both_decode_loops(tmp_path, monkeypatch):
     _trace(t, [(WIDE, 5, 300000.0), (COMPACT, 5, 310000.0)])
     with pytest.raises(SystemExit, match="several kernels"):
         bench.main(["--config", "c1", "--ingest-profile", t, t, t, t, t])
+
+
+def test_cache_and_latency_counters_are_summarised(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t, f, w, cf, cw, hit, lat = (str(tmp_path / n) for n in ("t", "f", "w", "cf", "cw", "hit", "lat"))
+    _trace(t, [(WIDE, 4, 300000.0)])
+    _counter(f, [(WIDE, 100.0)])
+    _counter(w, [(WIDE, 100.0)])
+    _counter(cf, [(COPY, 524288.0)])
+    _counter(cw, [(COPY, 1048576.0)])
+    named = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write_csv(os.path.join(hit, "run_counter_collection.csv"), named,
+               [(WIDE, "TCC_HIT_sum", 30.0), (WIDE, "TCC_MISS_sum", 70.0), (WIDE, "TCC_HIT_sum", 30.0),
+                (WIDE, "TCC_MISS_sum", 70.0), (COPY, "TCC_HIT_sum", 1e9)])
+    _write_csv(os.path.join(lat, "run_counter_collection.csv"), named,
+               [(WIDE, "VmemLatency", 2500.0), (WIDE, "TCC_EA0_RDREQ_LEVEL_sum", 9000.0),
+                (WIDE, "TCC_EA0_RDREQ_sum", 10.0)])
+    assert bench.main(["--config", "c1", "--ingest-profile", t, f, w, cf, cw, "--extra-counters", hit, lat]) == 0
+    with open(tmp_path / "profiles" / "traffic.json") as fh:
+        e = json.load(fh)["c1/steps"]
+    assert e["l2_hit_rate"] == pytest.approx(0.3)
+    assert e["vmem_latency_cycles"] == pytest.approx(2500.0)
+    assert e["ea_read_latency_cycles"] == pytest.approx(900.0)
+    md = (tmp_path / "profiles" / "sdm_decode_steps_wide_kernel_c1.md").read_text()
+    assert "L2 hit rate" in md and "0.300" in md
