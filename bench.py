@@ -46,9 +46,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def launch_kind(config: str, entry: str) -> str:
-    """What one timed launch runs: the gather, the multi-token decode or the single step."""
-    return "gather" if config == "c3" else ("steps" if entry == "steps" else "step")
+def launch_kind(config: str, entry: str, gather: str = "two-ops") -> str:
+    """What one timed launch runs: the gather (or one of its other launch shapes), the
+    multi-token decode or the single step."""
+    if config == "c3":
+        return "gather" if gather == "two-ops" else f"gather-{gather}"
+    return "steps" if entry == "steps" else "step"
+
+
+def kernel_pattern(kind: str) -> str:
+    return KERNEL_PATTERN["gather" if kind.startswith("gather") else kind]
 
 
 # Name fragment that selects a launch kind's kernels in a rocprofv3 trace (the
@@ -81,6 +88,9 @@ def parse_args(argv=None):
     p.add_argument("--entry", default="steps", choices=["steps", "step"],
                    help="decode: one sdm_decode_steps launch per token sequence (steps), or one "
                         "sdm_decode_step launch per token (step)")
+    p.add_argument("--gather", default="two-ops", choices=["two-ops", "one-op", "no-stash", "one-op-no-stash"],
+                   help="gather launch shape on the c3 tokens: both operands with the stash (the workload), "
+                        "operand 0 only (the backward's gather), or either without the stash")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -251,26 +261,32 @@ def bench_gather(torch, args, cfg_name, wl):
     T = wl.tokens
     t = torch.arange(T, device=dev)
     live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
+    two = args.gather in ("two-ops", "no-stash")
+    with_stash = args.gather in ("two-ops", "one-op")
     out0 = torch.empty((T, wl.head_dim), device=dev)
-    out1 = torch.empty((T, wl.head_dim), device=dev)
-    stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev)
+    out1 = torch.empty((T, wl.head_dim), device=dev) if two else None
+    stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev) if with_stash else None
     torch.cuda.synchronize()
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.gather == "two-ops":
         cpu = cpu_baseline_gather(torch, wl, bank, inp, live, args.cpu_seconds, cfg_name)
     K = args.steps if args.steps is not None else 20
+    ops = dict(idx1=inp["idx1"], w1=inp["w1"], out1=out1) if two else {}
 
     def launch_one(i):
-        sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
-                   idx1=inp["idx1"], w1=inp["w1"], out0=out0, out1=out1, stash=stash)
+        sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"], out0=out0,
+                   stash=stash, with_stash=with_stash, **ops)
 
     ms = _run_steps(torch, args, launch_one, K)
     ms_step = ms / K
-    row_bytes = live * (wl.width0 + wl.width1) * wl.head_dim * es + T * wl.width0 * wl.head_dim * es
+    width_read = wl.width0 + (wl.width1 if two else 0)
+    row_bytes = live * width_read * wl.head_dim * es + (T * wl.width0 * wl.head_dim * es if with_stash else 0)
     gbps = row_bytes / (ms_step * 1e-3) / 1e9
-    config = {"workload": f"{cfg_name}: {wl.name}", "tokens": T, "live_tokens": live, "chunk": wl.chunk,
-              "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1], "slots": wl.num_slots,
-              "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "launch": args.launch, "seed": args.seed}
+    name = f"{cfg_name}: {wl.name}" + ("" if args.gather == "two-ops" else f" [{args.gather}]")
+    config = {"workload": name, "tokens": T, "live_tokens": live, "chunk": wl.chunk,
+              "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0], "stash": with_stash,
+              "slots": wl.num_slots, "bank_dtype": str(wl.bank_dtype).replace("torch.", ""),
+              "launch": args.launch, "seed": args.seed}
     value = T * K / (ms * 1e-3)
     return dict(value=value, unit="tokens/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
                 row_bytes=row_bytes, cpu=cpu, tokens_per_s=value)
@@ -352,8 +368,10 @@ def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
 
 def ingest_profile(args) -> int:
     trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
+    if args.config == "c3" and args.gather != "two-ops":
+        raise SystemExit("bench.py: profiles are summarised for the workload's own launch shape only")
     kind = launch_kind(args.config, args.entry)
-    pattern = KERNEL_PATTERN[kind]
+    pattern = kernel_pattern(kind)
     stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if pattern in r["Name"]]
     if not stats:
         raise SystemExit(f"bench.py: no {pattern} kernel in the trace under {trace}")
@@ -450,7 +468,7 @@ def main(argv=None):
         r = bench_decode(torch, args, args.config, wl)
     else:
         r = bench_gather(torch, args, args.config, wl)
-    kind = launch_kind(args.config, args.entry)
+    kind = launch_kind(args.config, args.entry, args.gather)
     traffic, kernel = stored_traffic(args.config, kind)
     out = {
         "metric": METRIC,
@@ -468,7 +486,7 @@ def main(argv=None):
         "config": r["config"],
         "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": kernel or KERNEL_PATTERN[kind], "algorithmic_bytes_per_launch": r["row_bytes"]},
+                     "kernel": kernel or kernel_pattern(kind), "algorithmic_bytes_per_launch": r["row_bytes"]},
         "cpu_baseline": r["cpu"],
         "tokens_per_s": r["tokens_per_s"],
         "row_gbps": r["gbps"],

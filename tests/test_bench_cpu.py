@@ -47,6 +47,9 @@ def test_launch_kinds():
     assert bench.launch_kind("c3", "steps") == "gather"
     assert bench.launch_kind("c1", "steps") == "steps"
     assert bench.launch_kind("c2", "step") == "step"
+    # the gather's other launch shapes never pick up the workload's stored traffic
+    assert bench.launch_kind("c3", "steps", "one-op") == "gather-one-op"
+    assert bench.kernel_pattern("gather-no-stash") == "sdm_gather_kernel"
 
 
 def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
