@@ -227,6 +227,34 @@ def test_power_of_two_scaling_is_exact():
     assert torch.equal(r2, r1 * 4) and torch.equal(b2, b1 * 4)
 
 
+def test_graph_of_single_steps_matches_eager():
+    """A sequence of single-step launches captured in one HIP graph (the benchmark's
+    --entry step path): every replay, from the same starting bank, equals eager steps."""
+    wl = gen.WORKLOADS["c1"].replace(streams=96, slots_per_stream=512, steps=6)
+    bank0 = gen.decode_bank(wl, 14).to(DEV)
+    seq = [{k: v.to(DEV) for k, v in gen.decode_step_inputs(wl, 14, t).items()} for t in range(wl.steps)]
+    ref_bank = bank0.clone()
+    ref = [sdm_decode_step(ref_bank, **inp) for inp in seq]
+    bank = bank0.clone()
+    outs = [torch.empty_like(r) for r in ref]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for inp, o in zip(seq, outs):
+            sdm_decode_step(bank, **inp, readings=o)
+    for i in range(3):
+        bank.copy_(bank0)
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16)), f"replay {i}, step {t}"
+        assert torch.equal(bank.view(torch.int16), ref_bank.view(torch.int16)), f"replay {i}"
+        del junk
+
+
 def test_zero_streams_and_errors_from_python():
     from sparse_delta_rule_amd import SdmError
     bank = torch.zeros(64, 8, device=DEV)

@@ -157,3 +157,62 @@ def test_full_size_c3():
     assert bits_equal(to_np_bank(stash[sample]), ref_st)
     del bank, stash
     torch.cuda.empty_cache()
+
+
+def test_graph_replays_match_eager():
+    """The benchmark's launch path: sdm_gather captured in a HIP graph. Every replay, with
+    eager torch work and synchronisations between replays and the outputs cleared
+    first, must equal an eager launch bit for bit."""
+    wl = gen.WORKLOADS["c3"].replace(num_slots=50000, tokens=1024)
+    bank = gen.gather_bank(wl, 21, DEV)
+    inp = gen.gather_inputs(wl, 21, DEV)
+    kw = dict(chunk=wl.chunk, chunk_valid=inp["chunk_valid"], idx1=inp["idx1"], w1=inp["w1"])
+    r0, rs, r1 = sdm_gather(bank, inp["idx0"], inp["w0"], **kw)
+    out0, stash, out1 = torch.empty_like(r0), torch.empty_like(rs), torch.empty_like(r1)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sdm_gather(bank, inp["idx0"], inp["w0"], **kw, out0=out0, out1=out1, stash=stash)
+    for i in range(3):
+        out0.fill_(7.0)
+        out1.fill_(7.0)
+        stash.fill_(7.0)
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out0.view(torch.int32), r0.view(torch.int32)), f"replay {i}"
+        assert torch.equal(out1.view(torch.int32), r1.view(torch.int32)), f"replay {i}"
+        assert torch.equal(stash.view(torch.int16), rs.view(torch.int16)), f"replay {i}"
+        del junk
+
+
+def test_debug_validation_catches_broken_preconditions():
+    """SDM_DEBUG_VALIDATE=1 in a child process: a slot outside the bank and a per-chunk
+    valid count above the chunk are reported before any launch."""
+    import os
+    import subprocess
+    import sys
+    code = r'''
+import torch, sparse_delta_rule_amd as sdm
+dev = torch.device("cuda", 0)
+bank = torch.zeros(100, 8, device=dev)
+def call(idx, cv):
+    idx = torch.tensor(idx, dtype=torch.int32, device=dev)
+    cv = torch.tensor(cv, dtype=torch.int32, device=dev)
+    try:
+        sdm.sdm_gather(bank, idx, torch.ones(idx.shape, device=dev), chunk=2, chunk_valid=cv)
+        torch.cuda.synchronize()
+        return "ok"
+    except sdm.SdmError as e:
+        return str(e)
+print(call([[1, 2], [3, 4]], [2]))
+print(call([[1, 2], [3, 100]], [2]))
+print(call([[1, 2], [3, 4]], [3]))
+'''
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SDM_DEBUG_VALIDATE="1")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120, cwd=root)
+    lines = out.stdout.strip().splitlines()
+    assert lines[0] == "ok", out.stderr
+    assert "outside [0, 100)" in lines[1]
+    assert "chunk_valid[0] = 3 outside [0, 2]" in lines[2]
