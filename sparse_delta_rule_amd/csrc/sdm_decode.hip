@@ -22,13 +22,17 @@
 // request all R rows into the same registers (one phase's rows at a time keeps
 // occupancy high); readings.
 //
-// sdm_decode_steps_kernel (T steps of one stream in one launch): the same step
-// in a loop, software-pipelined so each step costs one wait for rows instead of
-// two plus a launch: right after the barrier that publishes step t's writes,
-// the R rows of step t and the W rows of step t + 1 are requested together
-// (both may be rows step t wrote, which that barrier orders), with step t + 2's
-// slots and weights; both weighted sums come out of one pass, and a step takes
-// three workgroup barriers.
+// sdm_decode_steps_kernel and sdm_decode_steps_wide_kernel (T steps of one
+// stream in one launch): the same step in a loop, software-pipelined so each
+// step costs one wait for rows instead of two plus a launch: right after the
+// barrier that publishes step t's writes, the R rows of step t and the W rows of
+// step t + 1 are requested together (both may be rows step t wrote, which that
+// barrier orders), with later steps' slots and weights. The compact loop, for
+// grids that keep many waves on each SIMD, sums step t + 1's rows in the next
+// iteration (fewer live registers) and takes five barriers per step; the wide
+// loop, for grids that leave at most two waves on each SIMD, forms both sums in
+// one pass, stages metadata two steps ahead and takes three barriers per step.
+// Both give the same results, bit for bit, as T single steps.
 //
 // This is an HBM-bound gather/scatter (about 1 flop per byte): vector memory
 // and VALU FMAs, no MFMA.
