@@ -37,12 +37,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP kernel sources; stored HBM-traffic figures are valid only for it."""
+    """Hash of the HIP kernel sources' code (comments and whitespace removed); stored
+    HBM-traffic figures are valid only for it."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "sparse_delta_rule_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(os.path.basename(p).encode())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
