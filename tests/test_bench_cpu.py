@@ -109,3 +109,15 @@ def test_cache_and_latency_counters_are_summarised(tmp_path, monkeypatch):
     assert e["ea_read_latency_cycles"] == pytest.approx(900.0)
     md = (tmp_path / "profiles" / "sdm_decode_steps_wide_kernel_c1.md").read_text()
     assert "L2 hit rate" in md and "0.300" in md
+
+
+def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    src = tmp_path / "sparse_delta_rule_amd" / "csrc"
+    src.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (src / "k.hip").write_text("// a kernel\nint f(int x) { return x + 1; }  /* one */\n")
+    h0 = bench.kernel_source_hash()
+    (src / "k.hip").write_text("// the kernel, reworded\n\nint f(int x) {\n  return x + 1;  // one\n}\n")
+    assert bench.kernel_source_hash() == h0
+    (src / "k.hip").write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash() != h0
