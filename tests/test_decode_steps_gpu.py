@@ -91,6 +91,9 @@ CASES = [
     ("hd129 f32 two slices", torch.float32, 5, 64, 129, 9, 33, 9, torch.int64, torch.float32, 5),
     ("hd300 bf16 three slices", torch.bfloat16, 4, 64, 300, 12, 12, 1, torch.int32, torch.bfloat16, 4),
     ("hd64 f32 W=1 R=64", torch.float32, 11, 128, 64, 1, 64, 1, torch.int32, torch.float32, 7),
+    # 64-thread workgroups for 128 columns: several metadata items per thread, over 5 tokens
+    ("hd128 bf16 W=R=16 G=W, 4 metadata items per thread", torch.bfloat16, 8, 64, 128, 16, 16, 16, torch.int32,
+     torch.float32, 5),
 ]
 
 
