@@ -127,48 +127,55 @@ int fetch_slots(const void* dev, int dtype, int64_t n, std::vector<int64_t>& out
     hipError_t e;
     if (dtype == SDM_I64) {
         e = hipMemcpyAsync(out.data(), dev, size_t(n) * 8, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
     } else {
         std::vector<int32_t> tmp(static_cast<size_t>(n));
         e = hipMemcpyAsync(tmp.data(), dev, size_t(n) * 4, hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
-        for (int64_t i = 0; i < n; ++i) out[size_t(i)] = tmp[size_t(i)];
+        if (e == hipSuccess)
+            for (int64_t i = 0; i < n; ++i) out[size_t(i)] = tmp[size_t(i)];
     }
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fail(SDM_E_HIP, "copying %s to the host: %s", name, hipGetErrorString(e));
     return SDM_OK;
 }
 
-int validate_decode_slots(int64_t num_slots, int64_t streams, int W, int R, const void* k_idx, int kd,
-                          const void* q_idx, int qd, hipStream_t stream) {
+// The slot preconditions of a decode call, over all of its tokens: every slot in
+// [0, num_slots), a stream's W write slots of a token distinct, and every slot
+// touched (written or read) by one stream only, across all tokens, since the
+// tokens of different streams run in no fixed order relative to one another.
+int validate_decode_slots(int64_t num_slots, int64_t steps, int64_t streams, int W, int R, const void* k_idx,
+                          int kd, const void* q_idx, int qd, hipStream_t stream) {
     std::vector<int64_t> k, q;
-    int rc = fetch_slots(k_idx, kd, streams * W, k, stream, "k_idx");
+    int rc = fetch_slots(k_idx, kd, steps * streams * W, k, stream, "k_idx");
     if (rc != SDM_OK) return rc;
-    rc = fetch_slots(q_idx, qd, streams * R, q, stream, "q_idx");
+    rc = fetch_slots(q_idx, qd, steps * streams * R, q, stream, "q_idx");
     if (rc != SDM_OK) return rc;
     std::unordered_map<int64_t, int64_t> owner;
     owner.reserve(size_t(streams) * size_t(W + R));
-    for (int64_t s = 0; s < streams; ++s) {
-        for (int w = 0; w < W; ++w) {
-            const int64_t x = k[size_t(s * W + w)];
-            if (x < 0 || x >= num_slots)
-                return fail(SDM_E_RANGE, "k_idx[%lld, %d] = %lld outside [0, %lld)", (long long)s, w,
-                            (long long)x, (long long)num_slots);
-            for (int u = 0; u < w; ++u)
-                if (k[size_t(s * W + u)] == x)
-                    return fail(SDM_E_RANGE, "stream %lld writes slot %lld twice", (long long)s, (long long)x);
-        }
-        for (int r = 0; r < R; ++r) {
-            const int64_t x = q[size_t(s * R + r)];
-            if (x < 0 || x >= num_slots)
-                return fail(SDM_E_RANGE, "q_idx[%lld, %d] = %lld outside [0, %lld)", (long long)s, r,
-                            (long long)x, (long long)num_slots);
-        }
-        for (int i = 0; i < W + R; ++i) {
-            const int64_t x = i < W ? k[size_t(s * W + i)] : q[size_t(s * R + i - W)];
-            auto it = owner.emplace(x, s);
-            if (!it.second && it.first->second != s)
-                return fail(SDM_E_RANGE, "slot %lld is used by streams %lld and %lld", (long long)x,
-                            (long long)it.first->second, (long long)s);
+    for (int64_t t = 0; t < steps; ++t) {
+        for (int64_t s = 0; s < streams; ++s) {
+            const int64_t* ks = k.data() + (t * streams + s) * W;
+            const int64_t* qs = q.data() + (t * streams + s) * R;
+            for (int w = 0; w < W; ++w) {
+                if (ks[w] < 0 || ks[w] >= num_slots)
+                    return fail(SDM_E_RANGE, "token %lld: k_idx[%lld, %d] = %lld outside [0, %lld)", (long long)t,
+                                (long long)s, w, (long long)ks[w], (long long)num_slots);
+                for (int u = 0; u < w; ++u)
+                    if (ks[u] == ks[w])
+                        return fail(SDM_E_RANGE, "token %lld: stream %lld writes slot %lld twice", (long long)t,
+                                    (long long)s, (long long)ks[w]);
+            }
+            for (int r = 0; r < R; ++r)
+                if (qs[r] < 0 || qs[r] >= num_slots)
+                    return fail(SDM_E_RANGE, "token %lld: q_idx[%lld, %d] = %lld outside [0, %lld)", (long long)t,
+                                (long long)s, r, (long long)qs[r], (long long)num_slots);
+            for (int i = 0; i < W + R; ++i) {
+                const int64_t x = i < W ? ks[i] : qs[i - W];
+                auto it = owner.emplace(x, s);
+                if (!it.second && it.first->second != s)
+                    return fail(SDM_E_RANGE, "token %lld: slot %lld is used by streams %lld and %lld", (long long)t,
+                                (long long)x, (long long)it.first->second, (long long)s);
+            }
         }
     }
     return SDM_OK;
@@ -256,14 +263,8 @@ int decode_call(const char* fn, void* bank, int bank_dtype, int64_t num_slots, i
             int rc = check_device_ptr(r.p, r.name);
             if (rc != SDM_OK) return rc;
         }
-        const int kb = elem_size(k_idx_dtype), qb = elem_size(q_idx_dtype);
-        for (int64_t t = 0; t < steps; ++t) {
-            int rc = validate_decode_slots(num_slots, streams, W, R,
-                                           static_cast<const char*>(k_idx) + t * streams * W * kb, k_idx_dtype,
-                                           static_cast<const char*>(q_idx) + t * streams * R * qb, q_idx_dtype,
-                                           stream);
-            if (rc != SDM_OK) return rc;
-        }
+        int rc = validate_decode_slots(num_slots, steps, streams, W, R, k_idx, k_idx_dtype, q_idx, q_idx_dtype, stream);
+        if (rc != SDM_OK) return rc;
     }
 
     int cus = 0, force = -1;

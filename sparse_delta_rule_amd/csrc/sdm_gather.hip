@@ -83,10 +83,9 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const bool lane_on = t < p.tokens && vi < p.vpr;
     const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
 
-    // LDS: slots [op][token][ch], weights [op][token][ch], then one live flag per token.
+    // LDS: slots [op][token][ch], then weights [op][token][ch].
     IdxT* s_idx = reinterpret_cast<IdxT*>(s_raw);
     WT* s_w = reinterpret_cast<WT*>(s_idx + kStageEntries);
-    int* s_live = reinterpret_cast<int*>(s_w + kStageEntries);
 
     bool live = false;
     if (t < p.tokens) {
@@ -94,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         const int64_t limit = p.chunk_valid != nullptr ? int64_t(p.chunk_valid[chunk_no]) : p.valid;
         live = (t - chunk_no * p.chunk) < limit;
     }
-    if (lane == 0 && op == 0) s_live[g] = live ? 1 : 0;
 
     const E* bank = static_cast<const E*>(p.bank);
     const int width = op == 0 ? p.width0 : p.width1;
@@ -189,7 +187,7 @@ hipError_t launch_typed(const GatherParams& p, const GatherGeometry& geo, hipStr
     const int64_t blocks = (p.tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
     const dim3 grid(unsigned(blocks), unsigned(geo.slices));
     const dim3 block(kThreads);
-    const size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT)) + size_t(geo.tokens_per_block) * sizeof(int);
+    const size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT));
     hipLaunchKernelGGL((sdm_gather_kernel<E, VB, NOPS, IdxT, WT>), grid, block, lds, stream, p);
     return hipGetLastError();
 }

@@ -163,6 +163,46 @@ def test_unknown_loop_name_is_rejected(monkeypatch):
     torch.cuda.synchronize()
 
 
+def test_debug_validation_spans_tokens():
+    """SDM_DEBUG_VALIDATE=1 in a child process: a slot one stream uses at token 0
+    and another at token 1 is reported (the streams' tokens are not ordered
+    against one another), as are a repeated write slot and a slot out of range
+    at a later token; slots that stay with one stream across tokens pass."""
+    import os
+    import subprocess
+    import sys
+    code = r'''
+import torch, sparse_delta_rule_amd as sdm
+dev = torch.device("cuda", 0)
+bank = torch.zeros(64, 8, device=dev)
+def call(k, q):
+    k = torch.tensor(k, dtype=torch.int32, device=dev); q = torch.tensor(q, dtype=torch.int64, device=dev)
+    T, S, W = k.shape; R = q.shape[2]
+    try:
+        sdm.sdm_decode_steps(bank, k, torch.ones(T, S, W, device=dev), torch.ones(T, S, 8, device=dev),
+                             torch.ones(T, S, 1, device=dev), torch.zeros(T, S, 1, device=dev), q,
+                             torch.ones(T, S, R, device=dev))
+        torch.cuda.synchronize()
+        return "ok"
+    except sdm.SdmError as e:
+        return str(e)
+print(call([[[1, 2], [3, 4]], [[2, 5], [4, 6]]], [[[1], [4]], [[5], [6]]]))
+print(call([[[1, 2], [3, 4]], [[2, 5], [4, 6]]], [[[1], [4]], [[5], [2]]]))
+print(call([[[1, 2], [3, 4]], [[2, 2], [4, 6]]], [[[1], [4]], [[5], [6]]]))
+print(call([[[1, 2], [3, 4]], [[2, 5], [4, 6]]], [[[1], [4]], [[64], [6]]]))
+'''
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SDM_DEBUG_VALIDATE="1")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120,
+                         cwd=root)
+    lines = out.stdout.strip().splitlines()
+    assert len(lines) == 4, out.stderr
+    assert lines[0] == "ok", lines[0]
+    assert "token 1: slot 2 is used by streams 0 and 1" in lines[1]
+    assert "token 1: stream 0 writes slot 2 twice" in lines[2]
+    assert "token 1: q_idx[0, 0] = 64 outside [0, 64)" in lines[3]
+
+
 def test_graph_replays_match_eager(loop):
     """The benchmark's launch path: sdm_decode_steps captured in a HIP graph. Every
     replay, with eager torch work and synchronisations between replays, must equal an
