@@ -132,7 +132,7 @@ def sdm_decode_step(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor
         raise ValueError("readings must be shaped like v, in the bank dtype")
     _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
                q_val=q_val, readings=readings)
-    streams = k_idx.numel() // W
+    streams = k_idx.numel() // W if W else 0  # W = 0 is left to the library to reject
     rc = library().sdm_decode_step(
         _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, streams, W, R, G,
         _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
@@ -174,7 +174,7 @@ def sdm_decode_steps(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tenso
     _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
                q_val=q_val, readings=readings)
     steps = lead[0]
-    streams = k_idx.numel() // (W * steps) if steps else 0
+    streams = k_idx.numel() // (W * steps) if W and steps else 0  # W = 0: rejected by the library
     rc = library().sdm_decode_steps(
         _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, steps, streams, W, R, G,
         _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
@@ -219,8 +219,19 @@ def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chun
         out1 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
     if stash is None and with_stash:
         stash = torch.empty((tokens, W0, hd), dtype=bank.dtype, device=dev)
-    if chunk_valid is not None and chunk_valid.dtype != torch.int32:
-        raise TypeError("chunk_valid must be int32")
+    # The library sees only pointers: a given output must have the extent it will write.
+    for name, t in (("out0", out0), ("out1", out1)):
+        if t is not None and (tuple(t.shape) != (tokens, hd) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [{tokens}, {hd}], got {t.dtype} {tuple(t.shape)}")
+    if stash is not None and (tuple(stash.shape) != (tokens, W0, hd) or stash.dtype != bank.dtype):
+        raise ValueError(f"stash must be {bank.dtype} [{tokens}, {W0}, {hd}], got {stash.dtype} "
+                         f"{tuple(stash.shape)}")
+    if chunk_valid is not None:
+        if chunk_valid.dtype != torch.int32:
+            raise TypeError("chunk_valid must be int32")
+        if chunk >= 1 and tokens % chunk == 0 and tuple(chunk_valid.shape) != (tokens // chunk,):
+            raise ValueError(f"chunk_valid must be [{tokens // chunk}] (one count per chunk), got "
+                             f"{tuple(chunk_valid.shape)}")
     _dev_check(dev, bank=bank, idx0=idx0, w0=w0, out0=out0, stash=stash, chunk_valid=chunk_valid,
                idx1=idx1, w1=w1, out1=out1)
     rc = library().sdm_gather(

@@ -239,3 +239,26 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("SDM_LIBRARY", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _binding.library()
+
+
+def test_python_binding_checks_the_extent_of_given_outputs():
+    """The library writes through plain pointers, so the binding checks that a
+    caller's output, stash and per-chunk count arrays have the extent it assumes
+    (these checks come before the device check, so CPU tensors reach them)."""
+    import torch
+    bank = torch.zeros(16, 4)
+    idx = torch.zeros(6, 2, dtype=torch.int32)
+    w = torch.zeros(6, 2)
+    with pytest.raises(ValueError, match="out0 must be float32"):
+        sdm.sdm_gather(bank, idx, w, chunk=3, out0=torch.zeros(6, 3), with_stash=False)
+    with pytest.raises(ValueError, match="out1 must be float32"):
+        sdm.sdm_gather(bank, idx, w, chunk=3, idx1=idx, w1=w, out1=torch.zeros(6, 4, dtype=torch.float64),
+                       with_stash=False)
+    with pytest.raises(ValueError, match="stash must be"):
+        sdm.sdm_gather(bank, idx, w, chunk=3, stash=torch.zeros(6, 1, 4))
+    with pytest.raises(ValueError, match="stash must be"):
+        sdm.sdm_gather(bank, idx, w, chunk=3, stash=torch.zeros(6, 2, 4, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="chunk_valid must be \\[2\\]"):
+        sdm.sdm_gather(bank, idx, w, chunk=3, chunk_valid=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="is on cpu"):  # right extents: on to the device check
+        sdm.sdm_gather(bank, idx, w, chunk=3, chunk_valid=torch.zeros(2, dtype=torch.int32))

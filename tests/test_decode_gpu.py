@@ -268,6 +268,10 @@ def test_zero_streams_and_errors_from_python():
     with pytest.raises(SdmError, match="SDM_E_RANGE"):
         sdm_decode_step(bank, idx, val, torch.zeros(1, 8, device=DEV), torch.zeros(1, 1, device=DEV),
                         torch.zeros(1, 1, device=DEV), idx, val)
+    z = torch.zeros(2, 0, dtype=torch.int64, device=DEV)  # W = R = 0
+    with pytest.raises(SdmError, match="SDM_E_RANGE"):
+        sdm_decode_step(bank, z, torch.zeros(2, 0, device=DEV), torch.zeros(2, 8, device=DEV),
+                        torch.zeros(2, 1, device=DEV), torch.zeros(2, 1, device=DEV), z, torch.zeros(2, 0, device=DEV))
 
 
 def test_debug_validation_catches_broken_preconditions():

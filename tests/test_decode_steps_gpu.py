@@ -145,6 +145,11 @@ def test_zero_tokens_and_errors():
     with pytest.raises(SdmError, match="SDM_E_RANGE"):
         sdm_decode_steps(bank, idx, val, torch.zeros(2, 1, 8, device=DEV), torch.zeros(2, 1, 1, device=DEV),
                          torch.zeros(2, 1, 1, device=DEV), idx, val)
+    z = torch.zeros(2, 3, 0, dtype=torch.int64, device=DEV)  # W = R = 0
+    with pytest.raises(SdmError, match="SDM_E_RANGE"):
+        sdm_decode_steps(bank, z, torch.zeros(2, 3, 0, device=DEV), torch.zeros(2, 3, 8, device=DEV),
+                         torch.zeros(2, 3, 1, device=DEV), torch.zeros(2, 3, 1, device=DEV), z,
+                         torch.zeros(2, 3, 0, device=DEV))
 
 
 def test_unknown_loop_name_is_rejected(monkeypatch):
