@@ -236,6 +236,60 @@ def test_float32_within_error_bound_of_float64(bf16, groups):
         assert np.all(np.abs(widen(bank64[case["k_idx"]]) - row_exact) <= ulp(row_exact, bf16) / 2)
 
 
+def _order_case(rows_w, rows_r, groups):
+    """float32 bank [rows_w; rows_r] (hd 1): write slots 0..W-1 with k_val = 1, g = 0,
+    beta = 1, v = 0 (so delta_v = -retrieved and each written row becomes
+    row - retrieved); read the untouched rows W.. with q_val = 1 (readings = their sum)."""
+    W, R = len(rows_w), len(rows_r)
+    bank = np.array([[x] for x in rows_w + rows_r], np.float32)
+    r = oracle.decode_step(bank, np.arange(W)[None], np.ones((1, W), np.float32), np.zeros((1, 1), np.float32),
+                           np.ones((1, 1), np.float32), np.zeros((1, 1), np.float32), np.arange(W, W + R)[None],
+                           np.ones((1, R), np.float32), groups=groups)
+    return bank[:W, 0].tolist(), float(r[0, 0])
+
+
+def test_summation_order_is_the_stated_one():
+    """Values for which the decode's float32 sums (over w, and over r) depend on the
+    order: group j sums w = j, j + groups, ... ascending from +0, and the group
+    partials are added in group order from +0. Near 2^24 adding 1 is a tie, which
+    rounds to the even neighbour 2^24."""
+    big = 2.0 ** 24
+    # rows [2^24, 1, 1]: ((0 + 2^24) + 1) + 1 = 2^24 as one ascending chain and as three
+    # groups in group order; a descending order would give (1 + 1) + 2^24 = 2^24 + 2.
+    # delta_v = -2^24, so row 1 becomes 1 - 2^24 = -16777215 exactly (-16777216 after
+    # a sum of 2^24 + 2).
+    for groups in (1, 3):
+        rows, read = _order_case([big, 1.0, 1.0], [big, 1.0, 1.0], groups)
+        assert read == big
+        assert rows == [0.0, -16777215.0, -16777215.0]
+    # rows [2^24, 1, -2^24, 1]: one chain ((2^24 + 1) - 2^24) + 1 = 1; two strided groups
+    # (2^24 - 2^24) + (1 + 1) = 2; contiguous halves would give (2^24 + 1) + (-2^24 + 1) = 1.
+    rows, read = _order_case([big, 1.0, -big, 1.0], [big, 1.0, -big, 1.0], 1)
+    assert read == 1.0
+    # each row minus 1: 16777215, 0, -16777217 (a tie, to even: -16777216), 0
+    assert rows == [16777215.0, 0.0, -16777216.0, 0.0]
+    rows, read = _order_case([big, 1.0, -big, 1.0], [big, 1.0, -big, 1.0], 2)
+    assert read == 2.0
+    # each row minus 2: 16777214, -1, -16777218, -1 (all exact)
+    assert rows == [16777214.0, -1.0, -16777218.0, -1.0]
+
+
+def test_update_is_one_fused_multiply_add():
+    """The new row is fma(k_val, delta_v, row * d) with row * d rounded first: one
+    rounding for the k_val * delta_v term and the add. float32 bank, row = -1,
+    k_val = 1 + 2^-12, g = 0, beta = 1, v = 0: retrieved = -(1 + 2^-12) and
+    delta_v = 1 + 2^-12 exactly, and the exact k_val * delta_v = 1 + 2^-11 + 2^-24.
+    Fused, the row becomes 2^-11 + 2^-24; a product rounded on its own (a tie,
+    to the even 1 + 2^-11) would leave 2^-11."""
+    kv = np.float32(1.0 + 2.0 ** -12)
+    bank = np.array([[-1.0]], np.float32)
+    r = oracle.decode_step(bank, np.array([[0]]), np.array([[kv]], np.float32), np.zeros((1, 1), np.float32),
+                           np.ones((1, 1), np.float32), np.zeros((1, 1), np.float32), np.array([[0]]),
+                           np.ones((1, 1), np.float32))
+    assert bank[0, 0] == 2.0 ** -11 + 2.0 ** -24
+    assert r[0, 0] == 2.0 ** -11 + 2.0 ** -24  # read after the write, q_val = 1
+
+
 def test_groups_agree_on_exact_integers():
     """Small-integer data make every sum exact: every grouping gives the same bits,
     so a term dropped by the grouped order would show."""
