@@ -290,6 +290,22 @@ def test_update_is_one_fused_multiply_add():
     assert r[0, 0] == 2.0 ** -11 + 2.0 ** -24  # read after the write, q_val = 1
 
 
+def test_delta_rounds_the_difference_then_the_product():
+    """delta_v = beta * (v - retrieved) with two roundings, the difference first.
+    float32 bank rows [-2^-24, 0] both written with k_val = 1, g = 0, v = 1,
+    beta = 1 + 2^-23: retrieved = -2^-24, v - retrieved = 1 + 2^-24 rounds (a tie,
+    to even) to 1, so delta_v = 1 + 2^-23, which row 1 (0 + 1 * delta_v) shows.
+    One rounding of the exact beta (v - retrieved), or an fma form of it, would
+    give 1 + 2^-22. Row 0 becomes -2^-24 + delta_v = 1 + 2^-24, a tie rounding to 1."""
+    bank = np.array([[-(2.0 ** -24)], [0.0]], np.float32)
+    r = oracle.decode_step(bank, np.array([[0, 1]]), np.ones((1, 2), np.float32), np.ones((1, 1), np.float32),
+                           np.array([[1.0 + 2.0 ** -23]], np.float32), np.zeros((1, 1), np.float32),
+                           np.array([[1]]), np.ones((1, 1), np.float32))
+    assert bank[1, 0] == 1.0 + 2.0 ** -23
+    assert bank[0, 0] == 1.0
+    assert r[0, 0] == 1.0 + 2.0 ** -23
+
+
 def test_groups_agree_on_exact_integers():
     """Small-integer data make every sum exact: every grouping gives the same bits,
     so a term dropped by the grouped order would show."""
