@@ -306,6 +306,21 @@ def test_delta_rounds_the_difference_then_the_product():
     assert r[0, 0] == 1.0 + 2.0 ** -23
 
 
+def test_coefficient_is_rounded_before_the_products():
+    """coef = k_val * d is rounded to float32 before it multiplies the rows.
+    g = 2^-12 gives d = 1 + 2^-12 (exp(2^-12) exceeds it by about a quarter ulp);
+    k_val = 1 + 2^-12 makes k_val * d = 1 + 2^-11 + 2^-24, a tie rounding to
+    coef = 1 + 2^-11. Against row 0 = -(1 + 2^-23): coef * row rounds to
+    -(1 + 2^-11 + 2^-23), while one rounding of k_val * d * row, or k_val times a
+    rounded d * row, gives -(1 + 2^-11 + 2^-22). With v = 0 and beta = 1 the
+    second written row (0, k_val 1) becomes delta_v = -retrieved."""
+    bank = np.array([[-(1.0 + 2.0 ** -23)], [0.0]], np.float32)
+    oracle.decode_step(bank, np.array([[0, 1]]), np.array([[1.0 + 2.0 ** -12, 1.0]], np.float32),
+                       np.zeros((1, 1), np.float32), np.ones((1, 1), np.float32),
+                       np.array([[2.0 ** -12]], np.float32), np.array([[1]]), np.ones((1, 1), np.float32))
+    assert bank[1, 0] == 1.0 + 2.0 ** -11 + 2.0 ** -23
+
+
 def test_groups_agree_on_exact_integers():
     """Small-integer data make every sum exact: every grouping gives the same bits,
     so a term dropped by the grouped order would show."""
