@@ -10,6 +10,10 @@ float32 with low halves 0x8000 (a tie), 0x7fff, 0x8001 and 0xffff, so its
 rounding to the bank dtype on the way in sees ties as well. The rounding is
 the one the pages fix for the bank (round to nearest, ties to even); the
 oracle implements it bit by bit, and the comparison is bit for bit.
+
+Five worked float32 cases sit on ties of the other rounding points (the
+summation order, coef = k_val * d rounded first, delta_v's two roundings, the
+fused update): the kernel must reproduce the oracle there as well.
 """
 
 import numpy as np
@@ -85,3 +89,40 @@ def test_multi_step_ties(loop):
         ref = oracle.decode_step(ref_bank, **step_to_numpy(per[t]), groups=1)
         assert bits_equal(to_np_bank(readings[t]), ref), f"token {t}: readings differ from the oracle"
     assert bits_equal(to_np_bank(bank), ref_bank), "bank differs from the oracle"
+
+
+# Worked float32 cases on rounding ties (each settles one rounding point the pages
+# leave open: summation order, coef = k_val * d rounded first, delta_v's two
+# roundings, the fused update); hd 1, one stream. Fields: bank rows, k_idx,
+# k_val, g, beta, v, q_idx, q_val, expected bank rows after the step.
+_BIG = 2.0 ** 24
+WORKED = {
+    "ascending chain": ([_BIG, 1, 1, _BIG, 1, 1], [0, 1, 2], [1, 1, 1], 0.0, 1.0, 0.0, [3, 4, 5], [1, 1, 1],
+                        [0.0, -16777215.0, -16777215.0, _BIG, 1, 1]),
+    "cancelling chain": ([_BIG, 1, -_BIG, 1], [0, 1, 2, 3], [1, 1, 1, 1], 0.0, 1.0, 0.0, [0], [1],
+                         [16777215.0, 0.0, -16777216.0, 0.0]),
+    "fused update": ([-1.0], [0], [1 + 2.0 ** -12], 0.0, 1.0, 0.0, [0], [1], [2.0 ** -11 + 2.0 ** -24]),
+    "delta roundings": ([-(2.0 ** -24), 0.0], [0, 1], [1, 1], 0.0, 1 + 2.0 ** -23, 1.0, [1], [1],
+                        [1.0, 1 + 2.0 ** -23]),
+    "coef rounded first": ([-(1 + 2.0 ** -23), 0.0], [0, 1], [1 + 2.0 ** -12, 1], 2.0 ** -12, 1.0, 0.0, [1], [1],
+                           [None, 1 + 2.0 ** -11 + 2.0 ** -23]),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKED))
+def test_worked_float32_ties(name):
+    rows, k, kv, g, beta, v, q, qv, expect = WORKED[name]
+    bank = torch.tensor([[x] for x in rows], dtype=torch.float32)
+    inp = {"k_idx": torch.tensor([k], dtype=torch.int64), "k_val": torch.tensor([kv], dtype=torch.float32),
+           "v": torch.tensor([[v]], dtype=torch.float32), "beta": torch.tensor([[beta]], dtype=torch.float32),
+           "g": torch.tensor([[g]], dtype=torch.float32), "q_idx": torch.tensor([q], dtype=torch.int64),
+           "q_val": torch.tensor([qv], dtype=torch.float32)}
+    ref_bank = bank.numpy().copy()
+    ref = oracle.decode_step(ref_bank, **step_to_numpy(inp), groups=1)
+    for i, e in enumerate(expect):
+        if e is not None:
+            assert ref_bank[i, 0] == np.float32(e), f"oracle row {i}"
+    dbank = bank.to(DEV)
+    readings = sdm_decode_step(dbank, **{key: t.to(DEV) for key, t in inp.items()})
+    assert bits_equal(readings.cpu().numpy(), ref), "readings differ from the oracle"
+    assert bits_equal(dbank.cpu().numpy(), ref_bank), "bank differs from the oracle"
