@@ -31,7 +31,7 @@ _LIB = os.path.join(_HERE, "libsdm_oracle.so")
 _lib = None
 
 _ERRORS = {-1: "bad sizes or widths", -2: "slot out of range", -3: "repeated write slot in a stream",
-           -4: "out of memory"}
+           -4: "out of memory", -5: "compact-stash position past its block or named by two slots"}
 
 
 def build() -> str:
@@ -60,6 +60,7 @@ def _load():
     lib.sdm_oracle_gather.argtypes = [P, i32, i64, i64, i64, i64, i64, P, P, P, i32, P, P,
                                       P, P, i32, P, i32]
     lib.sdm_oracle_gather_f64.argtypes = [P, i32, i64, i64, i64, i64, i64, P, P, P, i32, P, P]
+    lib.sdm_oracle_gather_compact_stash.argtypes = [P, i32, i64, i64, i64, i64, i64, P, P, i32, P, P]
     lib.oracle_float_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_float_to_bf16.restype = ctypes.c_uint16
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
@@ -67,7 +68,7 @@ def _load():
     lib.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_float.restype = ctypes.c_float
     for f in (lib.sdm_oracle_decode_step, lib.sdm_oracle_decode_step_f64, lib.sdm_oracle_gather,
-              lib.sdm_oracle_gather_f64):
+              lib.sdm_oracle_gather_f64, lib.sdm_oracle_gather_compact_stash):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,6 +190,27 @@ def gather(bank, idx0, w0, *, chunk, valid=None, chunk_valid=None, idx1=None, w1
         W0, _ptr(out0), _ptr(st), _ptr(idx1), _ptr(w1), W1, _ptr(out1), groups)
     _check(rc, "gather")
     return out0, st, out1
+
+
+def gather_compact_stash(bank, idx0, kpos, stash, *, chunk, valid=None, chunk_valid=None):
+    """The compact stash of operand 0, written into ``stash`` [tokens / chunk,
+    chunk * width0, hd] (bank dtype) in place and returned: a live entry with
+    kpos >= 0 copies its row to that position of its chunk's block; other rows
+    keep their contents. The outputs are those of ``gather``."""
+    bf = _bank_kind(bank)
+    idx0 = _i64(idx0)
+    T, W0 = idx0.shape
+    kp = np.ascontiguousarray(kpos, dtype=np.int32)
+    assert kp.shape == (T, W0)
+    hd = bank.shape[1]
+    assert stash.dtype == bank.dtype and stash.flags.c_contiguous and stash.size == T * W0 * hd
+    if valid is None:
+        valid = chunk
+    cv = None if chunk_valid is None else np.ascontiguousarray(chunk_valid, dtype=np.int32)
+    rc = _load().sdm_oracle_gather_compact_stash(_ptr(bank), bf, bank.shape[0], hd, T, chunk, valid, _ptr(cv),
+                                                 _ptr(idx0), W0, _ptr(kp), _ptr(stash))
+    _check(rc, "gather_compact_stash")
+    return stash
 
 
 def gather_f64(bank, idx, w, *, chunk, valid=None, chunk_valid=None):

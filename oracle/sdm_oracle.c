@@ -56,6 +56,7 @@ enum {
     ORACLE_E_SLOT = -2,       /* slot outside [0, num_slots) */
     ORACLE_E_DUP = -3,        /* repeated write slot within one stream */
     ORACLE_E_NOMEM = -4,
+    ORACLE_E_POS = -5,        /* compact-stash position past its block, or named by two slots */
 };
 
 /* ---------------------------------------------------------------- bfloat16 */
@@ -345,6 +346,45 @@ int sdm_oracle_gather(const void* bank, int bank_bf16, int64_t num_slots, int64_
         }
     }
     free(rows);
+    return ORACLE_OK;
+}
+
+/* The compact stash (page "sparse_delta_memory/cuda/gather_cuda.py": the
+ * kernel's snapshot addressing when a position map kpos is given, and the host
+ * checks of token_gather_dc). The stash holds one block of chunk * width0 rows
+ * per chunk; entry n of a live token t of chunk k, with p = kpos[t, n] >= 0,
+ * copies the raw row bank[idx0[t, n]] to row p of block k. Entries with a
+ * negative position and every entry of a padding token copy nothing, and rows
+ * that no entry names keep their contents. Two live entries of one chunk that
+ * name one position must name one slot (which row would land there is not
+ * defined otherwise); both that and a position past the block are ORACLE_E_POS. The
+ * outputs are those of sdm_oracle_gather. */
+int sdm_oracle_gather_compact_stash(const void* bank, int bank_bf16, int64_t num_slots, int64_t hd, int64_t tokens,
+                                    int64_t chunk, int64_t valid, const int32_t* chunk_valid, const int64_t* idx0,
+                                    int width0, const int32_t* kpos, void* stash) {
+    int rc = check_gather_args(num_slots, hd, tokens, chunk, valid, chunk_valid, idx0, width0, NULL, 0, 1);
+    if (rc != ORACLE_OK) return rc;
+    const int es = bank_bf16 ? 2 : 4;
+    const int64_t crow = chunk * width0;
+    int64_t* owner = (int64_t*)malloc(sizeof(int64_t) * (size_t)crow);  /* slot stored at each position */
+    if (!owner) return ORACLE_E_NOMEM;
+    for (int64_t k = 0; k < tokens / chunk; ++k) {
+        for (int64_t p = 0; p < crow; ++p) owner[p] = -1;
+        for (int64_t t = k * chunk; t < (k + 1) * chunk; ++t) {
+            if (!token_live(t, chunk, valid, chunk_valid)) continue;
+            for (int n = 0; n < width0; ++n) {
+                const int64_t p = kpos[t * width0 + n];
+                if (p < 0) continue;
+                if (p >= crow) { free(owner); return ORACLE_E_POS; }
+                const int64_t slot = idx0[t * width0 + n];
+                if (owner[p] >= 0 && owner[p] != slot) { free(owner); return ORACLE_E_POS; }
+                owner[p] = slot;
+                memcpy((unsigned char*)stash + (size_t)((k * crow + p) * hd * es),
+                       (const unsigned char*)bank + (size_t)(slot * hd * es), (size_t)(hd * es));
+            }
+        }
+    }
+    free(owner);
     return ORACLE_OK;
 }
 

@@ -157,3 +157,75 @@ def test_bad_arguments_are_reported():
     idx[0, 0] = 4
     with pytest.raises(ValueError, match="out of range"):
         oracle.gather(bank, idx, w, chunk=3)
+
+
+# ------------------------------------------------------------ compact stash
+# Page "sparse_delta_memory/cuda/gather_cuda.py": with a position map kpos (one
+# int32 per entry of operand 0: its first position in the chunk's sorted row
+# list, or -1), the stash is one block of chunk * width0 rows per chunk and a
+# live entry copies its row to that position of its chunk's block; nothing
+# else is written.
+SENTINEL = 0x7E  # a byte pattern no copied row has
+
+
+def _sentinel_stash(T, W0, hd, dtype):
+    return np.full(T * W0 * hd * np.dtype(dtype).itemsize, SENTINEL, np.uint8).view(dtype).reshape(T, W0, hd)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_compact_stash_worked_example(bf16):
+    """Two chunks of two tokens, width 2. Chunk 0 (both live) names slots 3, 1, 1, 0;
+    sorted 0, 1, 1, 3, so the first positions are slot 0 -> 0, slot 1 -> 1,
+    slot 3 -> 3, and position 2 (the second 1) is never written. Chunk 1 has one
+    live token naming slot 2 twice (first position 0) and a padding token whose
+    entries carry positions that must not be used."""
+    bank = _bank([[1, 2], [3, 4], [5, 6], [7, 8]], bf16)
+    idx0 = np.array([[3, 1], [1, 0], [2, 2], [0, 3]])
+    kpos = np.array([[3, 1], [1, 0], [0, 0], [2, 3]], np.int32)
+    stash = _sentinel_stash(4, 2, 2, bank.dtype).reshape(2, 4, 2)
+    oracle.gather_compact_stash(bank, idx0, kpos, stash, chunk=2, chunk_valid=np.array([2, 1], np.int32))
+    untouched = _sentinel_stash(1, 1, 2, bank.dtype)[0, 0]
+    expect = [[bank[0], bank[1], untouched, bank[3]], [bank[2], untouched, untouched, untouched]]
+    for k in range(2):
+        for p in range(4):
+            assert bits_equal(stash[k, p], expect[k][p]), (k, p)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_compact_stash_with_identity_positions_is_the_full_stash(bf16):
+    """kpos = (t mod chunk) * width0 + n puts every entry where the full stash has
+    it: the live tokens' rows agree with the full stash, the padding tokens' rows
+    keep their contents (the full stash zeroes them), and -1 entries skip."""
+    rng = np.random.default_rng(41)
+    T, chunk, W0, hd = 24, 8, 5, 6
+    bank, idx, w = _rand(rng, T, W0, hd, 40, bf16)
+    cv = np.array([3, 0, 8], np.int32)
+    _, full, _ = oracle.gather(bank, idx, w, chunk=chunk, chunk_valid=cv)
+    kpos = ((np.arange(T) % chunk)[:, None] * W0 + np.arange(W0)[None, :]).astype(np.int32)
+    kpos[5, 2] = -1
+    kpos[20, 0] = -7  # any negative position stores nothing
+    stash = _sentinel_stash(T, W0, hd, bank.dtype)
+    oracle.gather_compact_stash(bank, idx, kpos, stash.reshape(T // chunk, chunk * W0, hd), chunk=chunk,
+                                chunk_valid=cv)
+    untouched = _sentinel_stash(1, 1, hd, bank.dtype)[0, 0]
+    for t in range(T):
+        live = (t % chunk) < cv[t // chunk]
+        for n in range(W0):
+            if live and kpos[t, n] >= 0:
+                assert bits_equal(stash[t, n], full[t, n]), (t, n)
+            else:
+                assert bits_equal(stash[t, n], untouched), (t, n)
+
+
+def test_compact_stash_rejects_conflicting_and_out_of_block_positions():
+    bank = np.arange(8, dtype=np.float32).reshape(4, 2)
+    idx0 = np.array([[0, 1], [2, 3]])
+    stash = np.zeros((1, 4, 2), np.float32)
+    with pytest.raises(ValueError, match="named by two slots"):  # slots 0 and 2 at position 1
+        oracle.gather_compact_stash(bank, idx0, np.array([[1, 0], [1, 2]], np.int32), stash, chunk=2)
+    with pytest.raises(ValueError, match="past its block"):
+        oracle.gather_compact_stash(bank, idx0, np.array([[0, 4], [1, 2]], np.int32), stash, chunk=2)
+    # one slot named twice at one position is fine; a padding token's conflict is not looked at
+    oracle.gather_compact_stash(bank, np.array([[0, 0], [2, 3]]), np.array([[0, 0], [0, 1]], np.int32), stash,
+                                chunk=2, valid=1)
+    assert bits_equal(stash[0, 0], bank[0])
