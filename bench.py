@@ -92,9 +92,11 @@ def parse_args(argv=None):
     p.add_argument("--entry", default="steps", choices=["steps", "step"],
                    help="decode: one sdm_decode_steps launch per token sequence (steps), or one "
                         "sdm_decode_step launch per token (step)")
-    p.add_argument("--gather", default="two-ops", choices=["two-ops", "one-op", "no-stash", "one-op-no-stash"],
+    p.add_argument("--gather", default="two-ops",
+                   choices=["two-ops", "one-op", "no-stash", "one-op-no-stash", "compact"],
                    help="gather launch shape on the c3 tokens: both operands with the stash (the workload), "
-                        "operand 0 only (the backward's gather), or either without the stash")
+                        "operand 0 only (the backward's gather), either without the stash, or both operands "
+                        "with a compact stash (sdm_gather_compact, positions from each chunk's sorted slots)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -257,7 +259,7 @@ def bench_decode(torch, args, cfg_name, wl):
 
 def bench_gather(torch, args, cfg_name, wl):
     import gen
-    from sparse_delta_rule_amd import sdm_gather
+    from sparse_delta_rule_amd import sdm_gather, sdm_gather_compact
     dev = torch.device("cuda", 0)
     es = torch.empty((), dtype=wl.bank_dtype).element_size()
     bank = gen.gather_bank(wl, args.seed, dev)
@@ -265,11 +267,19 @@ def bench_gather(torch, args, cfg_name, wl):
     T = wl.tokens
     t = torch.arange(T, device=dev)
     live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
-    two = args.gather in ("two-ops", "no-stash")
+    two = args.gather in ("two-ops", "no-stash", "compact")
     with_stash = args.gather in ("two-ops", "one-op")
+    compact = args.gather == "compact"
     out0 = torch.empty((T, wl.head_dim), device=dev)
     out1 = torch.empty((T, wl.head_dim), device=dev) if two else None
     stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev) if with_stash else None
+    if compact:
+        kpos = gen.compact_positions(inp["idx0"], wl.chunk, inp["chunk_valid"])
+        chunk_of = (torch.arange(T, device=dev) // wl.chunk)[:, None].expand_as(kpos)
+        stored = kpos >= 0
+        # rows the compact stash must hold: distinct (chunk, position) pairs
+        compact_rows = int(torch.unique(chunk_of[stored] * (wl.chunk * wl.width0) + kpos[stored].long()).numel())
+        stash = torch.empty((T // wl.chunk, wl.chunk * wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev)
     torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu_baseline and args.gather == "two-ops":
@@ -278,17 +288,23 @@ def bench_gather(torch, args, cfg_name, wl):
     ops = dict(idx1=inp["idx1"], w1=inp["w1"], out1=out1) if two else {}
 
     def launch_one(i):
-        sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"], out0=out0,
-                   stash=stash, with_stash=with_stash, **ops)
+        if compact:
+            sdm_gather_compact(bank, inp["idx0"], inp["w0"], kpos, chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+                               out0=out0, stash=stash, **ops)
+        else:
+            sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"], out0=out0,
+                       stash=stash, with_stash=with_stash, **ops)
 
     ms = _run_steps(torch, args, launch_one, K)
     ms_step = ms / K
     width_read = wl.width0 + (wl.width1 if two else 0)
-    row_bytes = live * width_read * wl.head_dim * es + (T * wl.width0 * wl.head_dim * es if with_stash else 0)
+    stash_rows = compact_rows if compact else (T * wl.width0 if with_stash else 0)
+    row_bytes = (live * width_read + stash_rows) * wl.head_dim * es
     gbps = row_bytes / (ms_step * 1e-3) / 1e9
     name = f"{cfg_name}: {wl.name}" + ("" if args.gather == "two-ops" else f" [{args.gather}]")
     config = {"workload": name, "tokens": T, "live_tokens": live, "chunk": wl.chunk,
-              "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0], "stash": with_stash,
+              "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0],
+              "stash": "compact" if compact else with_stash, "stash_rows": stash_rows,
               "slots": wl.num_slots, "bank_dtype": str(wl.bank_dtype).replace("torch.", ""),
               "launch": args.launch, "seed": args.seed}
     value = T * K / (ms * 1e-3)

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the sparse-delta-memory decode step and token gather.
 
 This package draws inputs only: banks, slot lists, weights, values, gates and
-chunk lengths. It holds none of the method's arithmetic, and both the oracle
+chunk lengths, and the compact-stash position map a caller derives from them. It holds none of the method's arithmetic, and both the oracle
 side and the HIP side of every test and benchmark take their inputs from it.
 """
 
@@ -9,6 +9,7 @@ from .workloads import (  # noqa: F401
     DecodeWorkload,
     GatherWorkload,
     WORKLOADS,
+    compact_positions,
     decode_bank,
     decode_step_inputs,
     decode_sequence,

@@ -252,3 +252,28 @@ def gather_inputs(wl: GatherWorkload, seed: int, device="cpu") -> dict:
                                        generator=_gen(device, seed, "valid"), device=device,
                                        dtype=torch.int32)
     return out
+
+
+def compact_positions(idx0: torch.Tensor, chunk: int, chunk_valid: torch.Tensor) -> torch.Tensor:
+    """A compact-stash position map for operand 0, as the pages' forward builds it:
+    within each chunk, the live tokens' entries are sorted by slot, and every
+    entry gets the first position of its slot in that sorted list (entries with
+    one slot share a position; later positions of a repeated slot stay unused);
+    padding tokens' entries get -1. int32 [tokens, width0], on idx0's device."""
+    T, W0 = idx0.shape
+    dev = idx0.device
+    if T == 0:
+        return torch.empty((0, W0), dtype=torch.int32, device=dev)
+    t = torch.arange(T, device=dev)
+    live = (t % chunk) < chunk_valid.to(dev).long()[t // chunk]
+    c = (t // chunk)[:, None].expand(T, W0)
+    slot = idx0.long()
+    # Sort key: chunk, then slot; padding entries sort after every live entry of their chunk.
+    big = int(slot.max()) + 2
+    key = c * (big + 1) + torch.where(live[:, None], slot, torch.full_like(slot, big))
+    flat = key.reshape(-1)
+    order = torch.sort(flat, stable=True).values
+    first = torch.searchsorted(order, flat)  # first position of the key in the sorted order
+    chunk_start = torch.searchsorted(order, (c.reshape(-1) * (big + 1)))  # where the chunk's block begins
+    pos = (first - chunk_start).reshape(T, W0)
+    return torch.where(live[:, None], pos, torch.full_like(pos, -1)).to(torch.int32)

@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 1
+#define SDM_ABI_VERSION 2 /* 2: adds sdm_gather_compact */
 #define SDM_MAX_WIDTH 256 /* largest W, R and gather width */
 
 /* Element types (sdm_dtype). */
@@ -184,6 +184,38 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
                const void* idx0, const void* w0, int32_t width0, float* out0, void* stash,
                const void* idx1, const void* w1, int32_t width1, float* out1,
                void* hip_stream);
+
+/*
+ * sdm_gather_compact: sdm_gather with a compact stash.
+ *
+ * Operation (page "sparse_delta_memory/cuda/gather_cuda.py": the kernel's
+ * snapshot addressing when a position map is passed, and the checks that
+ * token_gather_dc makes of that map). Outputs exactly as sdm_gather. The stash
+ * is one block of chunk * width0 rows per chunk, [tokens / chunk, chunk * width0,
+ * head_dim] in the bank dtype (as many bytes as sdm_gather's stash): entry n of a
+ * live token t with p = kpos[t, n] >= 0 copies the raw row bank[idx0[t, n]] to
+ * row p of the block of chunk t / chunk. Entries with a negative position and
+ * every entry of a padding token copy nothing, and rows that no entry names keep
+ * their contents (nothing is zeroed). On the pages the map gives each entry the
+ * first position of its slot in its chunk's sorted list of slots, so the block
+ * holds each distinct row once and entries with one slot share a position.
+ *
+ * Arguments: as sdm_gather, with
+ *   stash   required: [tokens / chunk, chunk * width0, head_dim] of bank_dtype.
+ *   kpos    required: [tokens, width0] int32 on the device.
+ * Preconditions (checked only under SDM_DEBUG_VALIDATE, with sdm_gather's): every
+ * position is below chunk * width0 (a position at or past it stores nothing);
+ * live entries of one chunk that name one position name one slot (otherwise
+ * which row lands there is not defined).
+ * Errors: as sdm_gather; SDM_E_NULL when tokens > 0 and stash or kpos is NULL.
+ */
+int sdm_gather_compact(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                       int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid,
+                       int idx_dtype, int w_dtype,
+                       const void* idx0, const void* w0, int32_t width0, float* out0,
+                       void* stash, const int32_t* kpos,
+                       const void* idx1, const void* w1, int32_t width1, float* out1,
+                       void* hip_stream);
 
 /* Message of the last failing call on this thread ("" if none). The pointer stays
  * valid until the next libsdm call on the same thread. */

@@ -60,6 +60,9 @@ def library() -> ctypes.CDLL:
     lib.sdm_gather.argtypes = [P, i32, i64, i64, i64, i64, i64, P, i32, i32, P, P, i32, P, P,
                                P, P, i32, P, P]
     lib.sdm_gather.restype = ctypes.c_int
+    lib.sdm_gather_compact.argtypes = [P, i32, i64, i64, i64, i64, i64, P, i32, i32, P, P, i32, P, P, P,
+                                       P, P, i32, P, P]
+    lib.sdm_gather_compact.restype = ctypes.c_int
     lib.sdm_last_error.argtypes = []
     lib.sdm_last_error.restype = ctypes.c_char_p
     lib.sdm_abi_version.argtypes = []
@@ -185,19 +188,10 @@ def sdm_decode_steps(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tenso
     return readings
 
 
-def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chunk: int,
-               valid: Optional[int] = None, chunk_valid: Optional[torch.Tensor] = None,
-               idx1: Optional[torch.Tensor] = None, w1: Optional[torch.Tensor] = None,
-               out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None,
-               stash: Optional[torch.Tensor] = None, with_stash: bool = True):
-    """Token gather (``sdm_gather`` of include/sdm.h). Returns (out0, stash, out1).
-
-    idx0, w0 [tokens, width0] (idx int32 or int64, weights float32 or bfloat16);
-    optional second operand idx1, w1 [tokens, width1]. ``valid`` defaults to
-    ``chunk``; ``chunk_valid`` (int32 [tokens / chunk]) overrides it per chunk.
-    out0/out1 [tokens, head_dim] float32 and stash [tokens, width0, head_dim] in the
-    bank dtype are allocated when not given (no stash if ``with_stash`` is False).
-    """
+def _gather_operands(bank, idx0, w0, chunk, valid, chunk_valid, idx1, w1, out0, out1, stash, stash_shape,
+                     make_stash):
+    """Shared checks and output allocation of the two gathers; returns the marshalled
+    argument head (bank .. out0, stash), the second operand's and the outputs."""
     if bank.dim() != 2 or idx0.dim() != 2 or tuple(w0.shape) != tuple(idx0.shape):
         raise ValueError("bank [slots, hd], idx0 and w0 [tokens, width0] expected")
     tokens, W0 = idx0.shape
@@ -217,15 +211,14 @@ def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chun
         out0 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
     if two and out1 is None:
         out1 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
-    if stash is None and with_stash:
-        stash = torch.empty((tokens, W0, hd), dtype=bank.dtype, device=dev)
+    if stash is None and make_stash is not None:
+        stash = make_stash(stash_shape, dtype=bank.dtype, device=dev)
     # The library sees only pointers: a given output must have the extent it will write.
     for name, t in (("out0", out0), ("out1", out1)):
         if t is not None and (tuple(t.shape) != (tokens, hd) or t.dtype != torch.float32):
             raise ValueError(f"{name} must be float32 [{tokens}, {hd}], got {t.dtype} {tuple(t.shape)}")
-    if stash is not None and (tuple(stash.shape) != (tokens, W0, hd) or stash.dtype != bank.dtype):
-        raise ValueError(f"stash must be {bank.dtype} [{tokens}, {W0}, {hd}], got {stash.dtype} "
-                         f"{tuple(stash.shape)}")
+    if stash is not None and (tuple(stash.shape) != stash_shape or stash.dtype != bank.dtype):
+        raise ValueError(f"stash must be {bank.dtype} {list(stash_shape)}, got {stash.dtype} {tuple(stash.shape)}")
     if chunk_valid is not None:
         if chunk_valid.dtype != torch.int32:
             raise TypeError("chunk_valid must be int32")
@@ -234,11 +227,57 @@ def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chun
                              f"{tuple(chunk_valid.shape)}")
     _dev_check(dev, bank=bank, idx0=idx0, w0=w0, out0=out0, stash=stash, chunk_valid=chunk_valid,
                idx1=idx1, w1=w1, out1=out1)
-    rc = library().sdm_gather(
-        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, tokens, chunk,
-        chunk if valid is None else valid, _ptr(chunk_valid), _dt(idx0, "idx0"), _dt(w0, "w0"),
-        _ptr(idx0), _ptr(w0), W0, _ptr(out0), _ptr(stash), _ptr(idx1), _ptr(w1), W1,
-        _ptr(out1), _stream_handle(dev))
+    head = (_ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, tokens, chunk, chunk if valid is None else valid,
+            _ptr(chunk_valid), _dt(idx0, "idx0"), _dt(w0, "w0"), _ptr(idx0), _ptr(w0), W0, _ptr(out0))
+    tail = (_ptr(idx1), _ptr(w1), W1, _ptr(out1), _stream_handle(dev))
+    return head, tail, out0, stash, out1
+
+
+def sdm_gather(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, chunk: int,
+               valid: Optional[int] = None, chunk_valid: Optional[torch.Tensor] = None,
+               idx1: Optional[torch.Tensor] = None, w1: Optional[torch.Tensor] = None,
+               out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None,
+               stash: Optional[torch.Tensor] = None, with_stash: bool = True):
+    """Token gather (``sdm_gather`` of include/sdm.h). Returns (out0, stash, out1).
+
+    idx0, w0 [tokens, width0] (idx int32 or int64, weights float32 or bfloat16);
+    optional second operand idx1, w1 [tokens, width1]. ``valid`` defaults to
+    ``chunk``; ``chunk_valid`` (int32 [tokens / chunk]) overrides it per chunk.
+    out0/out1 [tokens, head_dim] float32 and stash [tokens, width0, head_dim] in the
+    bank dtype are allocated when not given (no stash if ``with_stash`` is False).
+    """
+    shape = (idx0.shape[0], idx0.shape[1], bank.shape[-1]) if idx0.dim() == 2 else ()
+    head, tail, out0, stash, out1 = _gather_operands(bank, idx0, w0, chunk, valid, chunk_valid, idx1, w1, out0,
+                                                     out1, stash, shape, torch.empty if with_stash else None)
+    rc = library().sdm_gather(*head, _ptr(stash), *tail)
+    if rc != 0:
+        _raise(rc)
+    return out0, stash, out1
+
+
+def sdm_gather_compact(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, kpos: torch.Tensor, *,
+                       chunk: int, valid: Optional[int] = None, chunk_valid: Optional[torch.Tensor] = None,
+                       idx1: Optional[torch.Tensor] = None, w1: Optional[torch.Tensor] = None,
+                       out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None,
+                       stash: Optional[torch.Tensor] = None):
+    """Token gather with a compact stash (``sdm_gather_compact`` of include/sdm.h).
+    Returns (out0, stash, out1).
+
+    As ``sdm_gather``, with kpos int32 [tokens, width0]: a live entry with
+    kpos >= 0 stores its row at that row of its chunk's block of the stash
+    [tokens / chunk, chunk * width0, head_dim] (bank dtype; zero-filled when not
+    given); other entries and padding tokens store nothing.
+    """
+    if idx0.dim() != 2 or kpos.dtype != torch.int32 or tuple(kpos.shape) != tuple(idx0.shape):
+        raise ValueError("kpos must be int32 shaped like idx0 [tokens, width0]")
+    tokens, W0 = idx0.shape
+    if chunk < 1 or tokens % chunk:
+        raise ValueError(f"tokens ({tokens}) must be a multiple of chunk ({chunk})")
+    shape = (tokens // chunk, chunk * W0, bank.shape[-1])
+    head, tail, out0, stash, out1 = _gather_operands(bank, idx0, w0, chunk, valid, chunk_valid, idx1, w1, out0,
+                                                     out1, stash, shape, torch.zeros)
+    _dev_check(bank.device, kpos=kpos)
+    rc = library().sdm_gather_compact(*head, _ptr(stash), _ptr(kpos), *tail)
     if rc != 0:
         _raise(rc)
     return out0, stash, out1

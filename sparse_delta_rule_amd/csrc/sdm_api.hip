@@ -6,6 +6,7 @@
 // host checks), reported as status codes with a thread-local message instead of
 // exceptions. Everything cheap is checked on the host before the first HIP call.
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -204,6 +205,41 @@ int validate_gather_slots(int64_t num_slots, int64_t tokens, int64_t chunk, cons
     return SDM_OK;
 }
 
+// Compact-stash positions: each below chunk * width0, and live entries of one
+// chunk that name one position name one slot.
+int validate_compact_positions(int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid,
+                               const void* idx0, int width0, int idx_dtype, const int32_t* kpos,
+                               hipStream_t stream) {
+    std::vector<int64_t> slots;
+    int rc = fetch_slots(idx0, idx_dtype, tokens * width0, slots, stream, "idx0");
+    if (rc != SDM_OK) return rc;
+    const int64_t n = tokens * width0, chunks = tokens / chunk, crow = chunk * width0;
+    std::vector<int32_t> kp(static_cast<size_t>(n)), cv(static_cast<size_t>(chunk_valid ? chunks : 0));
+    hipError_t e = hipMemcpyAsync(kp.data(), kpos, size_t(n) * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess && chunk_valid != nullptr)
+        e = hipMemcpyAsync(cv.data(), chunk_valid, size_t(chunks) * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "copying kpos: %s", hipGetErrorString(e));
+    std::vector<int64_t> owner(static_cast<size_t>(crow));
+    for (int64_t c = 0; c < chunks; ++c) {
+        std::fill(owner.begin(), owner.end(), int64_t(-1));
+        const int64_t limit = chunk_valid ? int64_t(cv[size_t(c)]) : valid;
+        for (int64_t t = c * chunk; t < c * chunk + limit && t < (c + 1) * chunk; ++t)
+            for (int j = 0; j < width0; ++j) {
+                const int64_t i = t * width0 + j, p = kp[size_t(i)];
+                if (p < 0) continue;
+                if (p >= crow)
+                    return fail(SDM_E_RANGE, "kpos[%lld, %d] = %lld outside [-1, %lld)", (long long)t, j, (long long)p,
+                                (long long)crow);
+                if (owner[size_t(p)] >= 0 && owner[size_t(p)] != slots[size_t(i)])
+                    return fail(SDM_E_RANGE, "chunk %lld: position %lld is named by slots %lld and %lld", (long long)c,
+                                (long long)p, (long long)owner[size_t(p)], (long long)slots[size_t(i)]);
+                owner[size_t(p)] = slots[size_t(i)];
+            }
+    }
+    return SDM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,57 +361,62 @@ int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head
                        k_idx_dtype, k_val, v, q_val, val_dtype, beta, g, q_idx, q_idx_dtype, readings, hip_stream);
 }
 
-int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t tokens, int64_t chunk,
-               int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype, const void* idx0,
-               const void* w0, int32_t width0, float* out0, void* stash, const void* idx1, const void* w1,
-               int32_t width1, float* out1, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by sdm_gather (kpos NULL) and sdm_gather_compact.
+int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype,
+                const void* idx0, const void* w0, int32_t width0, float* out0, void* stash, const int32_t* kpos,
+                const void* idx1, const void* w1, int32_t width1, float* out1, void* hip_stream) {
     if (bank_dtype != SDM_F32 && bank_dtype != SDM_BF16)
-        return fail(SDM_E_DTYPE, "sdm_gather: bank must be float32 or bfloat16 (dtype %d)", bank_dtype);
+        return fail(SDM_E_DTYPE, "%s: bank must be float32 or bfloat16 (dtype %d)", fn, bank_dtype);
     if (idx_dtype != SDM_I32 && idx_dtype != SDM_I64)
-        return fail(SDM_E_DTYPE, "sdm_gather: indices must be int32 or int64 (dtype %d)", idx_dtype);
+        return fail(SDM_E_DTYPE, "%s: indices must be int32 or int64 (dtype %d)", fn, idx_dtype);
     if (w_dtype != SDM_F32 && w_dtype != SDM_BF16)
-        return fail(SDM_E_DTYPE, "sdm_gather: weights must be float32 or bfloat16 (dtype %d)", w_dtype);
+        return fail(SDM_E_DTYPE, "%s: weights must be float32 or bfloat16 (dtype %d)", fn, w_dtype);
     if (num_slots < 1 || head_dim < 1)
-        return fail(SDM_E_SHAPE, "sdm_gather: the bank needs at least one slot and one column, got [%lld, %lld]",
+        return fail(SDM_E_SHAPE, "%s: the bank needs at least one slot and one column, got [%lld, %lld]", fn,
                     (long long)num_slots, (long long)head_dim);
     if (tokens < 0 || chunk < 1 || tokens % chunk != 0 || valid < 0 || valid > chunk)
-        return fail(SDM_E_SHAPE, "sdm_gather: need tokens = k * chunk and 0 <= valid <= chunk, got tokens=%lld "
-                    "chunk=%lld valid=%lld", (long long)tokens, (long long)chunk, (long long)valid);
+        return fail(SDM_E_SHAPE, "%s: need tokens = k * chunk and 0 <= valid <= chunk, got tokens=%lld "
+                    "chunk=%lld valid=%lld", fn, (long long)tokens, (long long)chunk, (long long)valid);
     if (width0 < 1 || width0 > SDM_MAX_WIDTH)
-        return fail(SDM_E_RANGE, "sdm_gather: width0 must be in 1..%d, got %d", SDM_MAX_WIDTH, width0);
+        return fail(SDM_E_RANGE, "%s: width0 must be in 1..%d, got %d", fn, SDM_MAX_WIDTH, width0);
     const bool two = idx1 != nullptr || w1 != nullptr || out1 != nullptr || width1 != 0;
     if (two) {
         if (idx1 == nullptr || w1 == nullptr || out1 == nullptr)
-            return fail(SDM_E_NULL, "sdm_gather: idx1, w1 and out1 go together");
+            return fail(SDM_E_NULL, "%s: idx1, w1 and out1 go together", fn);
         if (width1 < 1 || width1 > SDM_MAX_WIDTH)
-            return fail(SDM_E_RANGE, "sdm_gather: width1 must be in 1..%d, got %d", SDM_MAX_WIDTH, width1);
+            return fail(SDM_E_RANGE, "%s: width1 must be in 1..%d, got %d", fn, SDM_MAX_WIDTH, width1);
     }
     const int es = elem_size(bank_dtype);
     if (!mul_fits(num_slots, head_dim, es) || !mul_fits(tokens, SDM_MAX_WIDTH, head_dim * 8))
-        return fail(SDM_E_SHAPE, "sdm_gather: sizes overflow 64-bit byte counts");
+        return fail(SDM_E_SHAPE, "%s: sizes overflow 64-bit byte counts", fn);
     if (tokens == 0) return ok();
     if (bank == nullptr || idx0 == nullptr || w0 == nullptr || out0 == nullptr)
-        return fail(SDM_E_NULL, "sdm_gather: bank, idx0, w0 and out0 are required");
+        return fail(SDM_E_NULL, "%s: bank, idx0, w0 and out0 are required", fn);
     const int is = elem_size(idx_dtype), ws = elem_size(w_dtype);
     if (!aligned(bank, es) || !aligned(idx0, is) || !aligned(w0, ws) || !aligned(out0, 4) ||
-        (stash != nullptr && !aligned(stash, es)) || !aligned(chunk_valid, 4) ||
+        (stash != nullptr && !aligned(stash, es)) || !aligned(chunk_valid, 4) || !aligned(kpos, 4) ||
         (two && (!aligned(idx1, is) || !aligned(w1, ws) || !aligned(out1, 4))))
-        return fail(SDM_E_ALIGN, "sdm_gather: a pointer is not aligned to its element size");
+        return fail(SDM_E_ALIGN, "%s: a pointer is not aligned to its element size", fn);
     const int64_t bank_bytes = num_slots * head_dim * es;
     const int64_t out_bytes = tokens * head_dim * 4;
     const int64_t stash_bytes = stash != nullptr ? tokens * width0 * head_dim * es : 0;
     if (overlap(out0, out_bytes, bank, bank_bytes) || overlap(stash, stash_bytes, bank, bank_bytes) ||
         (two && overlap(out1, out_bytes, bank, bank_bytes)))
-        return fail(SDM_E_OVERLAP, "sdm_gather: stash and outputs must not overlap the bank");
+        return fail(SDM_E_OVERLAP, "%s: stash and outputs must not overlap the bank", fn);
     if (overlap(out0, out_bytes, stash, stash_bytes) || (two && (overlap(out1, out_bytes, stash, stash_bytes) ||
                                                                  overlap(out0, out_bytes, out1, out_bytes))))
-        return fail(SDM_E_OVERLAP, "sdm_gather: stash and outputs must not overlap one another");
+        return fail(SDM_E_OVERLAP, "%s: stash and outputs must not overlap one another", fn);
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (debug_validate()) {
-        const void* ptrs[] = {bank, idx0, w0, out0, stash, chunk_valid, idx1, w1, out1};
-        const char* names[] = {"bank", "idx0", "w0", "out0", "stash", "chunk_valid", "idx1", "w1", "out1"};
-        for (int i = 0; i < 9; ++i) {
+        const void* ptrs[] = {bank, idx0, w0, out0, stash, chunk_valid, kpos, idx1, w1, out1};
+        const char* names[] = {"bank", "idx0", "w0", "out0", "stash", "chunk_valid", "kpos", "idx1", "w1", "out1"};
+        for (int i = 0; i < 10; ++i) {
             if (ptrs[i] == nullptr) continue;
             int rc = check_device_ptr(ptrs[i], names[i]);
             if (rc != SDM_OK) return rc;
@@ -383,6 +424,8 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
         int rc = validate_gather_slots(num_slots, tokens, chunk, chunk_valid, idx0, width0, idx_dtype, stream, "idx0");
         if (rc == SDM_OK && two)
             rc = validate_gather_slots(num_slots, tokens, chunk, nullptr, idx1, width1, idx_dtype, stream, "idx1");
+        if (rc == SDM_OK && kpos != nullptr)
+            rc = validate_compact_positions(tokens, chunk, valid, chunk_valid, idx0, width0, idx_dtype, kpos, stream);
         if (rc != SDM_OK) return rc;
     }
 
@@ -390,7 +433,7 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
                                                          reinterpret_cast<uintptr_t>(stash), two);
     const int64_t blocks = (tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
     if (blocks > 0x7fffffffLL || geo.slices > 65535)
-        return fail(SDM_E_SHAPE, "sdm_gather: %lld tokens x %d column slices exceed the grid", (long long)tokens,
+        return fail(SDM_E_SHAPE, "%s: %lld tokens x %d column slices exceed the grid", fn, (long long)tokens,
                     geo.slices);
     sdm::GatherParams p{};
     p.bank = bank;
@@ -402,6 +445,7 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
     p.w1 = two ? w1 : nullptr;
     p.out1 = two ? out1 : nullptr;
     p.chunk_valid = chunk_valid;
+    p.kpos = kpos;
     p.hd = head_dim;
     p.tokens = tokens;
     p.chunk = chunk;
@@ -414,8 +458,31 @@ int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head
     p.w_bf16 = w_dtype == SDM_BF16;
     p.out_vec = aligned(out0, 16) && (!two || aligned(out1, 16));
     hipError_t e = sdm::launch_gather(p, geo, bank_dtype == SDM_BF16, two, stream);
-    if (e != hipSuccess) return fail(SDM_E_HIP, "sdm_gather: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(SDM_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_gather(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t tokens, int64_t chunk,
+               int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype, const void* idx0,
+               const void* w0, int32_t width0, float* out0, void* stash, const void* idx1, const void* w1,
+               int32_t width1, float* out1, void* hip_stream) {
+    return gather_call("sdm_gather", bank, bank_dtype, num_slots, head_dim, tokens, chunk, valid, chunk_valid,
+                       idx_dtype, w_dtype, idx0, w0, width0, out0, stash, nullptr, idx1, w1, width1, out1, hip_stream);
+}
+
+int sdm_gather_compact(const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim, int64_t tokens,
+                       int64_t chunk, int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype,
+                       const void* idx0, const void* w0, int32_t width0, float* out0, void* stash, const int32_t* kpos,
+                       const void* idx1, const void* w1, int32_t width1, float* out1, void* hip_stream) {
+    if (tokens > 0 && (stash == nullptr || kpos == nullptr))
+        return fail(SDM_E_NULL, "sdm_gather_compact: stash and kpos are required");
+    return gather_call("sdm_gather_compact", bank, bank_dtype, num_slots, head_dim, tokens, chunk, valid,
+                       chunk_valid, idx_dtype, w_dtype, idx0, w0, width0, out0, stash, kpos, idx1, w1, width1, out1,
+                       hip_stream);
 }
 
 }  // extern "C"

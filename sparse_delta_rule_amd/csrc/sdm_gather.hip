@@ -24,6 +24,11 @@
 // it leaves two waves per SIMD), all of a batch's row loads issued before the
 // first is used. Padding tokens load no row. Rows are loaded and outputs and
 // stash rows stored non-temporally: all of them are touched once.
+//
+// Compact stash (CMP): operand 0's entry positions (kpos) are staged with its
+// slots and weights, and a live entry with a position p >= 0 stores its row at
+// row p of its chunk's block of chunk * width0 rows instead of at (t, n); other
+// entries and padding tokens store nothing.
 
 #include "sdm_kernels.h"
 
@@ -38,11 +43,13 @@ constexpr int kNB = 32;              // row loads in flight per lane (a power of
 // N consecutive entries [n0, n0 + N) of one operand, all valid: every row load
 // is issued before the first row is used, and each row feeds the sum
 // unconditionally (a row used only under a branch would have its load moved
-// next to that use and waited for there).
-template <typename E, int VB, int N, typename IdxT, typename WT>
+// next to that use and waited for there). stash_row: this token's stash rows,
+// or (CMP) its chunk's block of crow rows, whose row s_kp[k] an entry names (a
+// position outside [0, crow) stores nothing); NULL for none.
+template <typename E, int VB, int N, bool CMP, typename IdxT, typename WT>
 __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t hd, int64_t col, int n0, int k0,
-                                             const IdxT* s_idx, const WT* s_w, E* stash_row,
-                                             float (&acc)[VB / sizeof(E)]) {
+                                             const IdxT* s_idx, const WT* s_w, const int32_t* s_kp, E* stash_row,
+                                             int64_t crow, float (&acc)[VB / sizeof(E)]) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
     V r[N];
@@ -54,7 +61,14 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        if (stash_row != nullptr) store_stream(reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col), r[i]);
+        if constexpr (CMP) {
+            if (stash_row != nullptr) {
+                const int32_t kp = s_kp[k0 + i];
+                if (kp >= 0 && kp < crow) store_stream(reinterpret_cast<V*>(stash_row + int64_t(kp) * hd + col), r[i]);
+            }
+        } else if (stash_row != nullptr) {
+            store_stream(reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col), r[i]);
+        }
         E el[VEC];
         __builtin_memcpy(el, &r[i], VB);
 #pragma unroll
@@ -62,8 +76,8 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     }
 }
 
-// NOPS: operands (1 or 2).
-template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+// NOPS: operands (1 or 2). CMP: compact stash.
+template <typename E, int VB, int NOPS, bool CMP, typename IdxT, typename WT>
 __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams p) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
@@ -83,9 +97,11 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const bool lane_on = t < p.tokens && vi < p.vpr;
     const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
 
-    // LDS: slots [op][token][ch], then weights [op][token][ch].
+    // LDS: slots [op][token][ch], weights [op][token][ch], then (CMP) positions
+    // laid out like the slots (operand 0's part used).
     IdxT* s_idx = reinterpret_cast<IdxT*>(s_raw);
     WT* s_w = reinterpret_cast<WT*>(s_idx + kStageEntries);
+    int32_t* s_kp = reinterpret_cast<int32_t*>(s_w + kStageEntries);
 
     bool live = false;
     if (t < p.tokens) {
@@ -97,14 +113,16 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const E* bank = static_cast<const E*>(p.bank);
     const int width = op == 0 ? p.width0 : p.width1;
     float* out = op == 0 ? p.out0 : p.out1;
-    E* stash_row = p.stash != nullptr && op == 0 && lane_on ? static_cast<E*>(p.stash) + t * p.width0 * p.hd
-                                                            : nullptr;
+    // CMP: the block of crow rows of t's chunk; else t's own rows.
+    const int64_t crow = p.chunk * p.width0;
+    const int64_t stash_base = CMP ? t / p.chunk * crow * p.hd : t * p.width0 * p.hd;
+    E* stash_row = p.stash != nullptr && op == 0 && lane_on ? static_cast<E*>(p.stash) + stash_base : nullptr;
 
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
 
-    if (!live && stash_row != nullptr) {
+    if (!CMP && !live && stash_row != nullptr) {
         V zero;
         __builtin_memset(&zero, 0, VB);
         for (int n = 0; n < p.width0; ++n) store_stream(reinterpret_cast<V*>(stash_row + int64_t(n) * p.hd + col), zero);
@@ -118,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         __syncthreads();  // the previous chunk's entries consumed
         IdxT si[NOPS][kStageRounds];
         WT sw[NOPS][kStageRounds];
+        int32_t sk[kStageRounds];
 #pragma unroll
         for (int o = 0; o < NOPS; ++o) {
             const IdxT* idx = static_cast<const IdxT*>(o == 0 ? p.idx0 : p.idx1);
@@ -131,6 +150,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
                 const int64_t tok = min(t_first + tt, t_last);
                 si[o][r] = idx[tok * wd + n];
                 sw[o][r] = w[tok * wd + n];
+                if (CMP && o == 0) sk[r] = p.kpos[tok * wd + n];
             }
         }
 #pragma unroll
@@ -139,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
             for (int r = 0; r < kStageRounds / NOPS; ++r) {
                 s_idx[o * (kStageEntries / NOPS) + tid + r * kThreads] = si[o][r];
                 s_w[o * (kStageEntries / NOPS) + tid + r * kThreads] = sw[o][r];
+                if (CMP && o == 0) s_kp[tid + r * kThreads] = sk[r];
             }
         __syncthreads();
         if (!(live && lane_on)) continue;
@@ -150,24 +171,24 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         const int end = min(width, base + ch);
         int n = base;
         for (; n + kNB <= end; n += kNB)
-            gather_batch<E, VB, kNB>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+            gather_batch<E, VB, kNB, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
         if (n + 16 <= end) {
-            gather_batch<E, VB, 16>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+            gather_batch<E, VB, 16, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
             n += 16;
         }
         if (n + 8 <= end) {
-            gather_batch<E, VB, 8>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+            gather_batch<E, VB, 8, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
             n += 8;
         }
         if (n + 4 <= end) {
-            gather_batch<E, VB, 4>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+            gather_batch<E, VB, 4, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
             n += 4;
         }
         if (n + 2 <= end) {
-            gather_batch<E, VB, 2>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+            gather_batch<E, VB, 2, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
             n += 2;
         }
-        if (n < end) gather_batch<E, VB, 1>(bank, p.hd, col, n, k_base + n, s_idx, s_w, stash_row, acc);
+        if (n < end) gather_batch<E, VB, 1, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
     }
     if (!lane_on) return;
 
@@ -182,28 +203,30 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     }
 }
 
-template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+template <typename E, int VB, int NOPS, bool CMP, typename IdxT, typename WT>
 hipError_t launch_typed(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
     const int64_t blocks = (p.tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
     const dim3 grid(unsigned(blocks), unsigned(geo.slices));
     const dim3 block(kThreads);
-    const size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT));
-    hipLaunchKernelGGL((sdm_gather_kernel<E, VB, NOPS, IdxT, WT>), grid, block, lds, stream, p);
+    const size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT) + (CMP ? sizeof(int32_t) : 0));
+    hipLaunchKernelGGL((sdm_gather_kernel<E, VB, NOPS, CMP, IdxT, WT>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 
-template <typename E, int VB, int NOPS>
+template <typename E, int VB, int NOPS, bool CMP>
 hipError_t launch_ops(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
     if (p.idx64)
-        return p.w_bf16 ? launch_typed<E, VB, NOPS, int64_t, uint16_t>(p, geo, stream)
-                        : launch_typed<E, VB, NOPS, int64_t, float>(p, geo, stream);
-    return p.w_bf16 ? launch_typed<E, VB, NOPS, int32_t, uint16_t>(p, geo, stream)
-                    : launch_typed<E, VB, NOPS, int32_t, float>(p, geo, stream);
+        return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, int64_t, uint16_t>(p, geo, stream)
+                        : launch_typed<E, VB, NOPS, CMP, int64_t, float>(p, geo, stream);
+    return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, int32_t, uint16_t>(p, geo, stream)
+                    : launch_typed<E, VB, NOPS, CMP, int32_t, float>(p, geo, stream);
 }
 
 template <typename E, int VB>
 hipError_t launch_vb(const GatherParams& p, const GatherGeometry& geo, bool two, hipStream_t stream) {
-    return two ? launch_ops<E, VB, 2>(p, geo, stream) : launch_ops<E, VB, 1>(p, geo, stream);
+    if (p.kpos != nullptr)
+        return two ? launch_ops<E, VB, 2, true>(p, geo, stream) : launch_ops<E, VB, 1, true>(p, geo, stream);
+    return two ? launch_ops<E, VB, 2, false>(p, geo, stream) : launch_ops<E, VB, 1, false>(p, geo, stream);
 }
 
 int pow2_ceil(int64_t x) {

@@ -201,6 +201,7 @@ struct GatherParams {
     const void* w1;
     float* out1;
     const int32_t* chunk_valid;
+    const int32_t* kpos;  // NULL, or operand 0's compact-stash positions [tokens, width0]
     int64_t hd, tokens, chunk, valid;
     int width0, width1;
     int vpr;  // vectors per row

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_decode_steps",
-                                     "sdm_gather", "sdm_last_error"]
+                                     "sdm_gather", "sdm_gather_compact", "sdm_last_error"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -205,6 +205,36 @@ def test_gather_rejects(kw, code, text):
 
 def test_gather_zero_tokens_is_a_no_op():
     rc, msg = call_gather(tokens=0, bank=None, out0=None)
+    assert rc == OK and msg == ""
+
+
+def call_gather_compact(kpos=A + 1800 * MB, **kw):
+    a = gather_args(**kw)
+    lib = sdm.library()
+    rc = lib.sdm_gather_compact(a["bank"], a["bank_dtype"], a["num_slots"], a["head_dim"], a["tokens"], a["chunk"],
+                                a["valid"], a["chunk_valid"], a["idx_dtype"], a["w_dtype"], a["idx0"], a["w0"],
+                                a["width0"], a["out0"], a["stash"], kpos, a["idx1"], a["w1"], a["width1"],
+                                a["out1"], a["stream"])
+    return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(stash=None), E_NULL, "stash and kpos are required"),
+    (dict(kpos=None), E_NULL, "stash and kpos are required"),
+    (dict(kpos=A + 1800 * MB + 2), E_ALIGN, "aligned"),
+    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
+    (dict(width0=0), E_RANGE, "width0"),
+    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "overlap the bank"),
+])
+def test_gather_compact_rejects(kw, code, text):
+    rc, msg = call_gather_compact(**kw)
+    assert rc == code, msg
+    assert text in msg and msg.startswith("sdm_gather_compact:")
+
+
+def test_gather_compact_zero_tokens_is_a_no_op():
+    rc, msg = call_gather_compact(tokens=0, bank=None, out0=None, stash=None, kpos=None)
     assert rc == OK and msg == ""
 
 

@@ -57,3 +57,30 @@ def test_sub_seed_separates_keys():
     seen = {gen.sub_seed(0, "k_idx", t) for t in range(100)}
     seen |= {gen.sub_seed(0, "q_idx", t) for t in range(100)}
     assert len(seen) == 200
+
+
+def test_compact_positions_are_first_positions_in_each_chunks_sorted_slots():
+    """Within a chunk, live entries with one slot share a position, a smaller slot
+    gets a smaller position, a slot's position counts the live entries of smaller
+    slots in the chunk, and padding entries get -1."""
+    import torch
+    g = torch.Generator().manual_seed(5)
+    T, chunk, W0 = 48, 16, 7
+    idx0 = torch.randint(0, 40, (T, W0), generator=g)  # many repeats
+    cv = torch.tensor([16, 9, 0], dtype=torch.int32)
+    kp = gen.compact_positions(idx0, chunk, cv)
+    assert kp.dtype == torch.int32 and kp.shape == (T, W0)
+    for c in range(T // chunk):
+        rows = range(c * chunk, (c + 1) * chunk)
+        live = [t for t in rows if t - c * chunk < int(cv[c])]
+        slots = [int(idx0[t, n]) for t in live for n in range(W0)]
+        for t in rows:
+            for n in range(W0):
+                if t not in live:
+                    assert kp[t, n] == -1
+                else:
+                    s = int(idx0[t, n])
+                    assert kp[t, n] == sum(1 for x in slots if x < s), (t, n)
+    # the worked example of the oracle's pins
+    ex = gen.compact_positions(torch.tensor([[3, 1], [1, 0], [2, 2], [0, 3]]), 2, torch.tensor([2, 1], dtype=torch.int32))
+    assert ex.tolist() == [[3, 1], [1, 0], [0, 0], [-1, -1]]
