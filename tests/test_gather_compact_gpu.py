@@ -115,6 +115,37 @@ def test_c3_shape_4096_tokens():
     run_compact(wl, 24)
 
 
+def test_graph_replays_match_eager():
+    """sdm_gather_compact captured in a HIP graph: every replay, with eager torch work and
+    synchronisations between replays and the outputs and stash refilled first (rows
+    no entry names must come back as they were put), equals an eager launch bit for bit."""
+    wl = gen.WORKLOADS["c3"].replace(num_slots=2000, tokens=1024)
+    bank = gen.gather_bank(wl, 25, DEV)
+    inp = gen.gather_inputs(wl, 25, DEV)
+    kpos = gen.compact_positions(inp["idx0"], wl.chunk, inp["chunk_valid"])
+    kw = dict(chunk=wl.chunk, chunk_valid=inp["chunk_valid"], idx1=inp["idx1"], w1=inp["w1"])
+    shape = (wl.tokens // wl.chunk, wl.chunk * wl.width0, wl.head_dim)
+    r0, rs, r1 = sdm_gather_compact(bank, inp["idx0"], inp["w0"], kpos, **kw,
+                                    stash=_patterned(shape, wl.bank_dtype, DEV))
+    out0, out1 = torch.empty_like(r0), torch.empty_like(r1)
+    stash = _patterned(shape, wl.bank_dtype, DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sdm_gather_compact(bank, inp["idx0"], inp["w0"], kpos, **kw, out0=out0, out1=out1, stash=stash)
+    for i in range(3):
+        out0.fill_(7.0)
+        out1.fill_(7.0)
+        stash.view(torch.uint8).fill_(PATTERN)
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out0.view(torch.int32), r0.view(torch.int32)), f"replay {i}"
+        assert torch.equal(out1.view(torch.int32), r1.view(torch.int32)), f"replay {i}"
+        assert torch.equal(stash.view(torch.int16), rs.view(torch.int16)), f"replay {i}"
+        del junk
+
+
 def test_errors_from_python():
     bank = torch.zeros(10, 4, device=DEV)
     idx = torch.zeros(6, 2, dtype=torch.int32, device=DEV)
