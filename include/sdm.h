@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 2 /* 2: adds sdm_gather_compact */
+#define SDM_ABI_VERSION 2 /* 2: adds sdm_gather_compact and the gather plan */
 #define SDM_MAX_WIDTH 256 /* largest W, R and gather width */
 
 /* Element types (sdm_dtype). */
@@ -216,6 +216,58 @@ int sdm_gather_compact(const void* bank, int bank_dtype, int64_t num_slots, int6
                        void* stash, const int32_t* kpos,
                        const void* idx1, const void* w1, int32_t width1, float* out1,
                        void* hip_stream);
+
+/*
+ * sdm_gather_plan_init / sdm_gather_plan_launch: one gather checked once and
+ * launched many times, each launch on another window of slot rows.
+ *
+ * Operation (page "sparse_delta_memory/cuda/gather_cuda.py": the plan and step
+ * functions that follow token_gather_dc, which check a launch once at the
+ * largest row offset a step will use and then launch it per step with the row
+ * offset and valid replaced). sdm_gather_plan_init runs every check of
+ * sdm_gather, without a stash or per-chunk counts, for `tokens` tokens whose
+ * slots and weights are rows [row0, row0 + tokens) of idx0 and w0 (and idx1, w1)
+ * for any row0 in [0, row0_max], and stores the launch in *plan. Then
+ *     sdm_gather_plan_launch(plan, row0, valid, hip_stream)
+ * gives, bit for bit, what
+ *     sdm_gather(bank, ..., tokens, chunk, valid, NULL, idx_dtype, w_dtype,
+ *                idx0 + row0 * width0, w0 + row0 * width0, width0, out0, NULL,
+ *                idx1 + row0 * width1, w1 + row0 * width1, width1, out1, hip_stream)
+ * gives (pointer steps in elements), checking only the plan, row0, valid and
+ * that the current device is the plan's. Every launch writes the same out0 and
+ * out1; padding is (t mod chunk) >= valid with t counted from the launch's
+ * first token, as in sdm_gather.
+ *
+ * The plan is a plain caller-owned struct (the library allocates nothing). It
+ * holds raw device pointers, so the caller keeps every array it names alive and
+ * in place while using the plan; a copy of the struct is the same plan. Launches
+ * are asynchronous on hip_stream and may be captured in a HIP graph (a captured
+ * launch keeps the row0 and valid it was captured with).
+ *
+ * Arguments of sdm_gather_plan_init: as sdm_gather without valid, chunk_valid
+ * and stash, and
+ *   plan       where the plan is stored (zeroed first, so a failed init leaves
+ *              no usable plan).
+ *   row0_max   >= 0: idx0 and w0 (idx1 and w1) hold row0_max + tokens rows.
+ * Under SDM_DEBUG_VALIDATE init checks the slots of all row0_max + tokens rows
+ * (copying them on the null stream).
+ * Errors of init: as sdm_gather; SDM_E_NULL for a NULL plan; SDM_E_HIP when the
+ * current device cannot be queried. Errors of launch: SDM_E_NULL (NULL plan),
+ * SDM_E_SHAPE (not an initialised plan), SDM_E_RANGE (row0 outside
+ * [0, row0_max] or valid outside [0, chunk]), SDM_E_DEVICE (the current device
+ * is not the plan's), SDM_E_HIP (launch failure).
+ */
+typedef struct {
+    uint64_t opaque[48];
+} sdm_gather_plan;
+
+int sdm_gather_plan_init(sdm_gather_plan* plan, const void* bank, int bank_dtype, int64_t num_slots,
+                         int64_t head_dim, int64_t tokens, int64_t chunk, int64_t row0_max,
+                         int idx_dtype, int w_dtype,
+                         const void* idx0, const void* w0, int32_t width0, float* out0,
+                         const void* idx1, const void* w1, int32_t width1, float* out1);
+
+int sdm_gather_plan_launch(const sdm_gather_plan* plan, int64_t row0, int64_t valid, void* hip_stream);
 
 /* Message of the last failing call on this thread ("" if none). The pointer stays
  * valid until the next libsdm call on the same thread. */

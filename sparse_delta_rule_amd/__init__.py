@@ -9,9 +9,11 @@ every entry point raises if the library is not built or a call fails.
     readings = sdm_decode_steps(bank, k_idx, k_val, v, beta, g, q_idx, q_val)  # [steps, ...] inputs
     out0, stash, out1 = sdm_gather(bank, idx0, w0, chunk=64, valid=64, idx1=..., w1=...)
     out0, stash, out1 = sdm_gather_compact(bank, idx0, w0, kpos, chunk=64, idx1=..., w1=...)
+    plan = sdm_gather_plan(bank, idx0, w0, tokens=64, chunk=64); plan.launch(row0, valid)
 """
 
 from ._binding import (  # noqa: F401
+    GatherPlan,
     SDM_BF16,
     SDM_F32,
     SDM_I32,
@@ -25,4 +27,5 @@ from ._binding import (  # noqa: F401
     sdm_decode_steps,
     sdm_gather,
     sdm_gather_compact,
+    sdm_gather_plan,
 )

@@ -63,6 +63,10 @@ def library() -> ctypes.CDLL:
     lib.sdm_gather_compact.argtypes = [P, i32, i64, i64, i64, i64, i64, P, i32, i32, P, P, i32, P, P, P,
                                        P, P, i32, P, P]
     lib.sdm_gather_compact.restype = ctypes.c_int
+    lib.sdm_gather_plan_init.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, i32, P, P, i32, P, P, P, i32, P]
+    lib.sdm_gather_plan_init.restype = ctypes.c_int
+    lib.sdm_gather_plan_launch.argtypes = [P, i64, i64, P]
+    lib.sdm_gather_plan_launch.restype = ctypes.c_int
     lib.sdm_last_error.argtypes = []
     lib.sdm_last_error.restype = ctypes.c_char_p
     lib.sdm_abi_version.argtypes = []
@@ -281,3 +285,70 @@ def sdm_gather_compact(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor,
     if rc != 0:
         _raise(rc)
     return out0, stash, out1
+
+
+class GatherPlan:
+    """A gather checked once and launched per step (``sdm_gather_plan_init`` /
+    ``sdm_gather_plan_launch`` of include/sdm.h). Holds the plan bytes and the
+    tensors it names, so they stay alive while the plan does; the tensors must
+    not be resized or moved."""
+
+    _WORDS = 48
+
+    def __init__(self, tensors: tuple, device: torch.device, outputs: tuple):
+        self._plan = (ctypes.c_uint64 * self._WORDS)()
+        self._keep = tensors
+        self._device = device
+        self.out0, self.out1 = outputs
+
+    def launch(self, row0: int, valid: int):
+        """Gather tokens whose slots and weights are rows [row0, row0 + tokens) into
+        out0 (and out1), with padding (t mod chunk) >= valid; on torch's current stream."""
+        rc = library().sdm_gather_plan_launch(ctypes.byref(self._plan), int(row0), int(valid),
+                                              _stream_handle(self._device))
+        if rc != 0:
+            _raise(rc)
+        return self.out0, self.out1
+
+
+def sdm_gather_plan(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *, tokens: int, chunk: int,
+                    idx1: Optional[torch.Tensor] = None, w1: Optional[torch.Tensor] = None,
+                    out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None) -> GatherPlan:
+    """Plan a gather of ``tokens`` tokens (no stash) whose slot and weight rows are
+    a window of idx0, w0 [rows, width0] (and idx1, w1): ``plan.launch(row0, valid)``
+    for any 0 <= row0 <= rows - tokens equals ``sdm_gather`` on rows
+    [row0, row0 + tokens) with that valid, written to the plan's out0 / out1."""
+    if bank.dim() != 2 or idx0.dim() != 2 or tuple(w0.shape) != tuple(idx0.shape):
+        raise ValueError("bank [slots, hd], idx0 and w0 [rows, width0] expected")
+    rows, W0 = idx0.shape
+    if tokens < 0 or tokens > rows:
+        raise ValueError(f"tokens ({tokens}) must be in [0, {rows}] (the rows of idx0)")
+    hd = bank.shape[1]
+    dev = bank.device
+    two = idx1 is not None
+    if two != (w1 is not None):
+        raise ValueError("idx1 and w1 go together")
+    W1 = 0
+    if two:
+        if idx1.dim() != 2 or tuple(w1.shape) != tuple(idx1.shape) or idx1.shape[0] != rows:
+            raise ValueError("idx1 and w1 must be [rows, width1], with idx0's rows")
+        W1 = idx1.shape[1]
+        if idx1.dtype != idx0.dtype or w1.dtype != w0.dtype:
+            raise TypeError("both operands must share index and weight dtypes")
+    if out0 is None:
+        out0 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
+    if two and out1 is None:
+        out1 = torch.empty((tokens, hd), dtype=torch.float32, device=dev)
+    for name, t in (("out0", out0), ("out1", out1)):
+        if t is not None and (tuple(t.shape) != (tokens, hd) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [{tokens}, {hd}], got {t.dtype} {tuple(t.shape)}")
+    _dev_check(dev, bank=bank, idx0=idx0, w0=w0, out0=out0, idx1=idx1, w1=w1, out1=out1)
+    plan = GatherPlan((bank, idx0, w0, out0, idx1, w1, out1), dev, (out0, out1))
+    with torch.cuda.device(dev):
+        rc = library().sdm_gather_plan_init(
+            ctypes.byref(plan._plan), _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, tokens, chunk,
+            rows - tokens, _dt(idx0, "idx0"), _dt(w0, "w0"), _ptr(idx0), _ptr(w0), W0, _ptr(out0), _ptr(idx1),
+            _ptr(w1), W1, _ptr(out1))
+    if rc != 0:
+        _raise(rc)
+    return plan

@@ -365,11 +365,23 @@ int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head
 
 namespace {
 
-// Shared by sdm_gather (kpos NULL) and sdm_gather_compact.
-int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
-                int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype,
-                const void* idx0, const void* w0, int32_t width0, float* out0, void* stash, const int32_t* kpos,
-                const void* idx1, const void* w1, int32_t width1, float* out1, void* hip_stream) {
+// A checked gather launch: its parameter block and geometry; run == false when there
+// is nothing to launch (tokens == 0).
+struct GatherLaunch {
+    sdm::GatherParams p;
+    sdm::GatherGeometry geo;
+    int two, bf16, run;
+};
+
+// Every check of a gather call, then its launch parameters. index_rows: the rows of
+// idx and w the call may read (tokens for a call, more for a plan), which the
+// SDM_DEBUG_VALIDATE slot checks cover.
+int gather_prepare(const char* fn, const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                   int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid, int idx_dtype,
+                   int w_dtype, const void* idx0, const void* w0, int32_t width0, float* out0, void* stash,
+                   const int32_t* kpos, const void* idx1, const void* w1, int32_t width1, float* out1,
+                   int64_t index_rows, hipStream_t stream, GatherLaunch* out) {
+    out->run = 0;
     if (bank_dtype != SDM_F32 && bank_dtype != SDM_BF16)
         return fail(SDM_E_DTYPE, "%s: bank must be float32 or bfloat16 (dtype %d)", fn, bank_dtype);
     if (idx_dtype != SDM_I32 && idx_dtype != SDM_I64)
@@ -394,6 +406,7 @@ int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_sl
     const int es = elem_size(bank_dtype);
     if (!mul_fits(num_slots, head_dim, es) || !mul_fits(tokens, SDM_MAX_WIDTH, head_dim * 8))
         return fail(SDM_E_SHAPE, "%s: sizes overflow 64-bit byte counts", fn);
+    if (!mul_fits(index_rows, SDM_MAX_WIDTH, 8)) return fail(SDM_E_SHAPE, "%s: sizes overflow 64-bit byte counts", fn);
     if (tokens == 0) return ok();
     if (bank == nullptr || idx0 == nullptr || w0 == nullptr || out0 == nullptr)
         return fail(SDM_E_NULL, "%s: bank, idx0, w0 and out0 are required", fn);
@@ -412,7 +425,6 @@ int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_sl
                                                                  overlap(out0, out_bytes, out1, out_bytes))))
         return fail(SDM_E_OVERLAP, "%s: stash and outputs must not overlap one another", fn);
 
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (debug_validate()) {
         const void* ptrs[] = {bank, idx0, w0, out0, stash, chunk_valid, kpos, idx1, w1, out1};
         const char* names[] = {"bank", "idx0", "w0", "out0", "stash", "chunk_valid", "kpos", "idx1", "w1", "out1"};
@@ -421,9 +433,10 @@ int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_sl
             int rc = check_device_ptr(ptrs[i], names[i]);
             if (rc != SDM_OK) return rc;
         }
-        int rc = validate_gather_slots(num_slots, tokens, chunk, chunk_valid, idx0, width0, idx_dtype, stream, "idx0");
+        int rc = validate_gather_slots(num_slots, index_rows, chunk, chunk_valid, idx0, width0, idx_dtype, stream,
+                                       "idx0");
         if (rc == SDM_OK && two)
-            rc = validate_gather_slots(num_slots, tokens, chunk, nullptr, idx1, width1, idx_dtype, stream, "idx1");
+            rc = validate_gather_slots(num_slots, index_rows, chunk, nullptr, idx1, width1, idx_dtype, stream, "idx1");
         if (rc == SDM_OK && kpos != nullptr)
             rc = validate_compact_positions(tokens, chunk, valid, chunk_valid, idx0, width0, idx_dtype, kpos, stream);
         if (rc != SDM_OK) return rc;
@@ -435,7 +448,8 @@ int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_sl
     if (blocks > 0x7fffffffLL || geo.slices > 65535)
         return fail(SDM_E_SHAPE, "%s: %lld tokens x %d column slices exceed the grid", fn, (long long)tokens,
                     geo.slices);
-    sdm::GatherParams p{};
+    sdm::GatherParams& p = out->p;
+    p = sdm::GatherParams{};
     p.bank = bank;
     p.stash = stash;
     p.idx0 = idx0;
@@ -457,10 +471,41 @@ int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_sl
     p.idx64 = idx_dtype == SDM_I64;
     p.w_bf16 = w_dtype == SDM_BF16;
     p.out_vec = aligned(out0, 16) && (!two || aligned(out1, 16));
-    hipError_t e = sdm::launch_gather(p, geo, bank_dtype == SDM_BF16, two, stream);
+    out->geo = geo;
+    out->two = two;
+    out->bf16 = bank_dtype == SDM_BF16;
+    out->run = 1;
+    return SDM_OK;
+}
+
+// Shared by sdm_gather (kpos NULL) and sdm_gather_compact.
+int gather_call(const char* fn, const void* bank, int bank_dtype, int64_t num_slots, int64_t head_dim,
+                int64_t tokens, int64_t chunk, int64_t valid, const int32_t* chunk_valid, int idx_dtype, int w_dtype,
+                const void* idx0, const void* w0, int32_t width0, float* out0, void* stash, const int32_t* kpos,
+                const void* idx1, const void* w1, int32_t width1, float* out1, void* hip_stream) {
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    GatherLaunch g;
+    int rc = gather_prepare(fn, bank, bank_dtype, num_slots, head_dim, tokens, chunk, valid, chunk_valid, idx_dtype,
+                            w_dtype, idx0, w0, width0, out0, stash, kpos, idx1, w1, width1, out1, tokens, stream, &g);
+    if (rc != SDM_OK || !g.run) return rc == SDM_OK ? ok() : rc;
+    hipError_t e = sdm::launch_gather(g.p, g.geo, g.bf16 != 0, g.two != 0, stream);
     if (e != hipSuccess) return fail(SDM_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
+
+// The contents of an sdm_gather_plan: a checked launch, the offsets a step moves
+// the slot and weight pointers by, and the bounds a step is checked against.
+constexpr uint64_t kPlanMagic = 0x314e414c50534453ull;  // "SDSPLAN1"
+struct PlanImpl {
+    uint64_t magic;
+    GatherLaunch g;
+    int64_t row0_max;
+    int64_t chunk;  // valid's bound, also for a plan with nothing to launch
+    int64_t idx_row0, w_row0, idx_row1, w_row1;  // bytes per token row of idx0, w0, idx1, w1
+    int device;
+};
+static_assert(sizeof(PlanImpl) <= sizeof(sdm_gather_plan), "sdm_gather_plan is too small");
+static_assert(alignof(PlanImpl) <= alignof(sdm_gather_plan), "sdm_gather_plan is under-aligned");
 
 }  // namespace
 
@@ -483,6 +528,67 @@ int sdm_gather_compact(const void* bank, int bank_dtype, int64_t num_slots, int6
     return gather_call("sdm_gather_compact", bank, bank_dtype, num_slots, head_dim, tokens, chunk, valid,
                        chunk_valid, idx_dtype, w_dtype, idx0, w0, width0, out0, stash, kpos, idx1, w1, width1, out1,
                        hip_stream);
+}
+
+int sdm_gather_plan_init(sdm_gather_plan* plan, const void* bank, int bank_dtype, int64_t num_slots,
+                         int64_t head_dim, int64_t tokens, int64_t chunk, int64_t row0_max, int idx_dtype, int w_dtype,
+                         const void* idx0, const void* w0, int32_t width0, float* out0, const void* idx1,
+                         const void* w1, int32_t width1, float* out1) {
+    const char* fn = "sdm_gather_plan_init";
+    if (plan == nullptr) return fail(SDM_E_NULL, "%s: plan is NULL", fn);
+    std::memset(plan, 0, sizeof *plan);
+    if (row0_max < 0) return fail(SDM_E_SHAPE, "%s: row0_max = %lld < 0", fn, (long long)row0_max);
+    if (tokens >= 0 && row0_max > INT64_MAX - tokens)
+        return fail(SDM_E_SHAPE, "%s: row0_max + tokens overflows", fn);
+    PlanImpl pl{};
+    // Checked at the largest valid; every step's valid is checked against the chunk.
+    int rc = gather_prepare(fn, bank, bank_dtype, num_slots, head_dim, tokens, chunk, chunk, nullptr, idx_dtype,
+                            w_dtype, idx0, w0, width0, out0, nullptr, nullptr, idx1, w1, width1, out1,
+                            tokens >= 0 ? row0_max + tokens : 0, nullptr, &pl.g);
+    if (rc != SDM_OK) return rc;
+    if (pl.g.run) {
+        const hipError_t e = hipGetDevice(&pl.device);
+        if (e != hipSuccess) return fail(SDM_E_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    }
+    const int is = elem_size(idx_dtype), ws = elem_size(w_dtype);
+    pl.row0_max = row0_max;
+    pl.chunk = chunk;
+    pl.idx_row0 = int64_t(width0) * is;
+    pl.w_row0 = int64_t(width0) * ws;
+    pl.idx_row1 = pl.g.two ? int64_t(width1) * is : 0;
+    pl.w_row1 = pl.g.two ? int64_t(width1) * ws : 0;
+    pl.magic = kPlanMagic;
+    std::memcpy(plan, &pl, sizeof pl);
+    return ok();
+}
+
+int sdm_gather_plan_launch(const sdm_gather_plan* plan, int64_t row0, int64_t valid, void* hip_stream) {
+    const char* fn = "sdm_gather_plan_launch";
+    if (plan == nullptr) return fail(SDM_E_NULL, "%s: plan is NULL", fn);
+    PlanImpl pl;
+    std::memcpy(&pl, plan, sizeof pl);
+    if (pl.magic != kPlanMagic) return fail(SDM_E_SHAPE, "%s: not an initialised gather plan", fn);
+    if (row0 < 0 || row0 > pl.row0_max)
+        return fail(SDM_E_RANGE, "%s: row0 = %lld outside [0, %lld]", fn, (long long)row0, (long long)pl.row0_max);
+    if (valid < 0 || valid > pl.chunk)
+        return fail(SDM_E_RANGE, "%s: valid = %lld outside [0, %lld]", fn, (long long)valid, (long long)pl.chunk);
+    if (!pl.g.run) return ok();
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SDM_E_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev != pl.device)
+        return fail(SDM_E_DEVICE, "%s: the plan is for device %d, the current device is %d", fn, pl.device, dev);
+    sdm::GatherParams p = pl.g.p;
+    p.idx0 = static_cast<const char*>(p.idx0) + row0 * pl.idx_row0;
+    p.w0 = static_cast<const char*>(p.w0) + row0 * pl.w_row0;
+    if (pl.g.two) {
+        p.idx1 = static_cast<const char*>(p.idx1) + row0 * pl.idx_row1;
+        p.w1 = static_cast<const char*>(p.w1) + row0 * pl.w_row1;
+    }
+    p.valid = valid;
+    e = sdm::launch_gather(p, pl.g.geo, pl.g.bf16 != 0, pl.g.two != 0, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SDM_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

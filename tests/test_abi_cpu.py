@@ -32,7 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_decode_steps",
-                                     "sdm_gather", "sdm_gather_compact", "sdm_last_error"]
+                                     "sdm_gather", "sdm_gather_compact", "sdm_gather_plan_init",
+                                     "sdm_gather_plan_launch", "sdm_last_error"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -236,6 +237,68 @@ def test_gather_compact_rejects(kw, code, text):
 def test_gather_compact_zero_tokens_is_a_no_op():
     rc, msg = call_gather_compact(tokens=0, bank=None, out0=None, stash=None, kpos=None)
     assert rc == OK and msg == ""
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("opaque", ctypes.c_uint64 * 48)]
+
+
+def plan_init(plan, **kw):
+    a = gather_args(**kw)
+    lib = sdm.library()
+    rc = lib.sdm_gather_plan_init(None if plan is None else ctypes.byref(plan), a["bank"], a["bank_dtype"],
+                                  a["num_slots"], a["head_dim"], a["tokens"], a["chunk"], a.get("row0_max", 100),
+                                  a["idx_dtype"], a["w_dtype"], a["idx0"], a["w0"], a["width0"], a["out0"],
+                                  a["idx1"], a["w1"], a["width1"], a["out1"])
+    return rc, lib.sdm_last_error().decode()
+
+
+def plan_launch(plan, row0, valid):
+    lib = sdm.library()
+    rc = lib.sdm_gather_plan_launch(None if plan is None else ctypes.byref(plan), row0, valid, None)
+    return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(row0_max=-1), E_SHAPE, "row0_max = -1"),
+    (dict(row0_max=(1 << 63) - 10), E_SHAPE, "overflows"),
+    (dict(bank_dtype=I64), E_DTYPE, "bank must be"),
+    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
+    (dict(width0=0), E_RANGE, "width0"),
+    (dict(idx1=None), E_NULL, "go together"),
+    (dict(out0=A + 1000 * 128), E_OVERLAP, "overlap the bank"),
+    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+])
+def test_gather_plan_init_rejects(kw, code, text):
+    plan = Plan()
+    plan.opaque[0] = 12345
+    rc, msg = plan_init(plan, **kw)
+    assert rc == code, msg
+    assert text in msg and msg.startswith("sdm_gather_plan_init:")
+    assert not any(plan.opaque), "a failed init leaves the plan zeroed"
+    rc, msg = plan_launch(plan, 0, 0)
+    assert rc == E_SHAPE and "not an initialised gather plan" in msg
+
+
+def test_gather_plan_null_and_range_checks():
+    rc, msg = plan_init(None)
+    assert rc == E_NULL and "plan is NULL" in msg
+    rc, msg = plan_launch(None, 0, 0)
+    assert rc == E_NULL and "plan is NULL" in msg
+    # an empty plan (tokens = 0) is made and launched without a device; its row0 and valid are still checked
+    plan = Plan()
+    rc, msg = plan_init(plan, tokens=0, chunk=16, row0_max=32, bank=None, out0=None)
+    assert rc == OK, msg
+    assert plan_launch(plan, 32, 16) == (OK, "")
+    rc, msg = plan_launch(plan, 33, 0)
+    assert rc == E_RANGE and "row0 = 33 outside [0, 32]" in msg
+    rc, msg = plan_launch(plan, -1, 0)
+    assert rc == E_RANGE and "row0 = -1" in msg
+    rc, msg = plan_launch(plan, 0, 17)
+    assert rc == E_RANGE and "valid = 17 outside [0, 16]" in msg
+    copy = Plan()
+    ctypes.memmove(ctypes.byref(copy), ctypes.byref(plan), ctypes.sizeof(Plan))
+    assert plan_launch(copy, 5, 3) == (OK, ""), "a copy of the struct is the same plan"
 
 
 def test_last_error_is_per_thread():
