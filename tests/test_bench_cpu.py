@@ -49,7 +49,9 @@ def test_launch_kinds():
     assert bench.launch_kind("c2", "step") == "step"
     # the gather's other launch shapes never pick up the workload's stored traffic
     assert bench.launch_kind("c3", "steps", "one-op") == "gather-one-op"
+    assert bench.launch_kind("c3", "steps", "compact") == "gather-compact"
     assert bench.kernel_pattern("gather-no-stash") == "sdm_gather_kernel"
+    assert bench.kernel_pattern("gather-compact") == "sdm_gather_kernel"
 
 
 def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
