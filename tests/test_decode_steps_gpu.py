@@ -132,6 +132,39 @@ def test_reads_of_next_tokens_writes_are_not_early(loop):
     check_steps(wl, 6, list(range(32)), edit=edit)
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_misaligned_bank_view_takes_narrow_vectors(dt, loop):
+    """A bank view one element past 16-byte alignment: the kernels read and write
+    rows with narrower vectors (element-wide here) and stay exact, multi-token
+    and single-token."""
+    wl = gen.DecodeWorkload(name="misaligned", bank_dtype=dt, streams=12, slots_per_stream=64, head_dim=128,
+                            W=16, R=16, G=16, steps=3, idx_dtype=torch.int64, weights="normal_sqrtw",
+                            beta="sigmoid", g_low=-0.1, bank_std=0.5)
+    bank0 = gen.decode_bank(wl, 61, "cpu")
+    seq = _sequence(wl, 61, "cpu", wl.steps)
+
+    def view():
+        full = torch.zeros(bank0.numel() + 1, dtype=dt, device=DEV)
+        b = full[1:].view(bank0.shape)
+        b.copy_(bank0.to(DEV))
+        assert b.data_ptr() % 16 != 0
+        return b
+
+    ref_bank = to_np_bank(bank0)
+    refs = [oracle.decode_step(ref_bank, **step_to_numpy({k: v[t] for k, v in seq.items()}),
+                               groups=documented_decode_groups(wl.W, wl.R)) for t in range(wl.steps)]
+    bank = view()
+    readings = sdm_decode_steps(bank, **seq)
+    for t in range(wl.steps):
+        assert bits_equal(to_np_bank(readings[t]), refs[t]), f"token {t}: readings differ from the oracle"
+    assert bits_equal(to_np_bank(bank), ref_bank), "bank differs from the oracle"
+    b1 = view()
+    for t in range(wl.steps):
+        r1 = sdm_decode_step(b1, **{k: v[t] for k, v in seq.items()})
+        assert bits_equal(to_np_bank(r1), refs[t]), f"single step {t}"
+    assert bits_equal(to_np_bank(b1), ref_bank)
+
+
 def test_zero_tokens_and_errors():
     from sparse_delta_rule_amd import SdmError
     bank = torch.zeros(64, 8, device=DEV)
