@@ -173,7 +173,9 @@ int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head
  *   stash        NULL (no copy), or [tokens, width0, head_dim] of bank_dtype.
  *   idx1, w1, out1, width1: the second operand, like the first; all NULL with
  *                width1 = 0 for one operand, or all given with width1 in 1..SDM_MAX_WIDTH.
- * Slots must lie in [0, num_slots) (checked only under SDM_DEBUG_VALIDATE).
+ * Slots of live tokens must lie in [0, num_slots) (checked only under
+ * SDM_DEBUG_VALIDATE); a padding token's slots and weights are never read and may
+ * hold anything.
  * Outputs and stash must not overlap the bank or one another (SDM_E_OVERLAP).
  * Errors: SDM_E_DTYPE, SDM_E_SHAPE, SDM_E_RANGE, SDM_E_NULL, SDM_E_ALIGN,
  * SDM_E_OVERLAP, SDM_E_HIP.

@@ -283,6 +283,13 @@ int sdm_oracle_decode_step_f64(void* bank, int bank_bf16, int64_t num_slots, int
 
 /* ------------------------------------------------------------- token gather */
 
+static int token_live(int64_t t, int64_t chunk, int64_t valid, const int32_t* chunk_valid) {
+    int64_t lim = chunk_valid ? (int64_t)chunk_valid[t / chunk] : valid;
+    return (t % chunk) < lim;
+}
+
+/* Slots are checked for live tokens only: a padding token reads no row (its
+ * outputs and stash rows are zeros), so its slots may hold anything. */
 static int check_gather_args(int64_t num_slots, int64_t hd, int64_t tokens, int64_t chunk, int64_t valid,
                              const int32_t* chunk_valid, const int64_t* idx0, int width0,
                              const int64_t* idx1, int width1, int groups) {
@@ -294,17 +301,15 @@ static int check_gather_args(int64_t num_slots, int64_t hd, int64_t tokens, int6
     if (chunk_valid)
         for (int64_t k = 0; k < tokens / chunk; ++k)
             if (chunk_valid[k] < 0 || chunk_valid[k] > chunk) return ORACLE_E_ARG;
-    for (int64_t i = 0; i < tokens * width0; ++i)
-        if (idx0[i] < 0 || idx0[i] >= num_slots) return ORACLE_E_SLOT;
-    if (idx1)
-        for (int64_t i = 0; i < tokens * width1; ++i)
-            if (idx1[i] < 0 || idx1[i] >= num_slots) return ORACLE_E_SLOT;
+    for (int64_t t = 0; t < tokens; ++t) {
+        if (!token_live(t, chunk, valid, chunk_valid)) continue;
+        for (int n = 0; n < width0; ++n)
+            if (idx0[t * width0 + n] < 0 || idx0[t * width0 + n] >= num_slots) return ORACLE_E_SLOT;
+        if (idx1)
+            for (int n = 0; n < width1; ++n)
+                if (idx1[t * width1 + n] < 0 || idx1[t * width1 + n] >= num_slots) return ORACLE_E_SLOT;
+    }
     return ORACLE_OK;
-}
-
-static int token_live(int64_t t, int64_t chunk, int64_t valid, const int32_t* chunk_valid) {
-    int64_t lim = chunk_valid ? (int64_t)chunk_valid[t / chunk] : valid;
-    return (t % chunk) < lim;
 }
 
 /* One or two operands (idx1 == NULL: one). Weights come widened to float

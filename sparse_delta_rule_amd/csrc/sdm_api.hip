@@ -182,18 +182,19 @@ int validate_decode_slots(int64_t num_slots, int64_t steps, int64_t streams, int
     return SDM_OK;
 }
 
-int validate_gather_slots(int64_t num_slots, int64_t tokens, int64_t chunk, const int32_t* chunk_valid,
-                          const void* idx, int width, int idx_dtype, hipStream_t stream, const char* name) {
-    std::vector<int64_t> v;
-    int rc = fetch_slots(idx, idx_dtype, tokens * width, v, stream, name);
-    if (rc != SDM_OK) return rc;
-    for (int64_t i = 0; i < tokens * width; ++i)
-        if (v[size_t(i)] < 0 || v[size_t(i)] >= num_slots)
-            return fail(SDM_E_RANGE, "%s[%lld] = %lld outside [0, %lld)", name, (long long)i,
-                        (long long)v[size_t(i)], (long long)num_slots);
+// The gather's slot preconditions over `rows` rows of its slot arrays: the
+// per-chunk counts in [0, chunk], and the slots of every live row in
+// [0, num_slots), row i being live when i mod chunk is below chunk i / chunk's
+// count (chunk_valid), else below valid. A padding row is never read, so its
+// slots may hold anything. A plan passes valid = chunk: its windows can make
+// any row live.
+int validate_gather_slots(int64_t num_slots, int64_t rows, int64_t chunk, int64_t valid, const int32_t* chunk_valid,
+                          const void* idx0, int width0, const void* idx1, int width1, int idx_dtype,
+                          hipStream_t stream) {
+    std::vector<int32_t> cv;
     if (chunk_valid != nullptr) {
-        const int64_t chunks = tokens / chunk;
-        std::vector<int32_t> cv(static_cast<size_t>(chunks));
+        const int64_t chunks = rows / chunk;
+        cv.resize(static_cast<size_t>(chunks));
         hipError_t e = hipMemcpyAsync(cv.data(), chunk_valid, size_t(chunks) * 4, hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return fail(SDM_E_HIP, "copying chunk_valid: %s", hipGetErrorString(e));
@@ -201,6 +202,24 @@ int validate_gather_slots(int64_t num_slots, int64_t tokens, int64_t chunk, cons
             if (cv[size_t(c)] < 0 || cv[size_t(c)] > chunk)
                 return fail(SDM_E_RANGE, "chunk_valid[%lld] = %d outside [0, %lld]", (long long)c, cv[size_t(c)],
                             (long long)chunk);
+    }
+    const struct { const void* idx; int width; const char* name; } ops[] = {{idx0, width0, "idx0"},
+                                                                           {idx1, width1, "idx1"}};
+    for (const auto& op : ops) {
+        if (op.idx == nullptr) continue;
+        std::vector<int64_t> v;
+        int rc = fetch_slots(op.idx, idx_dtype, rows * op.width, v, stream, op.name);
+        if (rc != SDM_OK) return rc;
+        for (int64_t i = 0; i < rows; ++i) {
+            const int64_t limit = chunk_valid != nullptr ? int64_t(cv[size_t(i / chunk)]) : valid;
+            if (i % chunk >= limit) continue;
+            for (int n = 0; n < op.width; ++n) {
+                const int64_t x = v[size_t(i * op.width + n)];
+                if (x < 0 || x >= num_slots)
+                    return fail(SDM_E_RANGE, "%s[%lld, %d] = %lld outside [0, %lld)", op.name, (long long)i, n,
+                                (long long)x, (long long)num_slots);
+            }
+        }
     }
     return SDM_OK;
 }
@@ -433,10 +452,8 @@ int gather_prepare(const char* fn, const void* bank, int bank_dtype, int64_t num
             int rc = check_device_ptr(ptrs[i], names[i]);
             if (rc != SDM_OK) return rc;
         }
-        int rc = validate_gather_slots(num_slots, index_rows, chunk, chunk_valid, idx0, width0, idx_dtype, stream,
-                                       "idx0");
-        if (rc == SDM_OK && two)
-            rc = validate_gather_slots(num_slots, index_rows, chunk, nullptr, idx1, width1, idx_dtype, stream, "idx1");
+        int rc = validate_gather_slots(num_slots, index_rows, chunk, valid, chunk_valid, idx0, width0,
+                                       two ? idx1 : nullptr, width1, idx_dtype, stream);
         if (rc == SDM_OK && kpos != nullptr)
             rc = validate_compact_positions(tokens, chunk, valid, chunk_valid, idx0, width0, idx_dtype, kpos, stream);
         if (rc != SDM_OK) return rc;

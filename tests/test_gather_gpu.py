@@ -208,6 +208,20 @@ def call(idx, cv):
 print(call([[1, 2], [3, 4]], [2]))
 print(call([[1, 2], [3, 100]], [2]))
 print(call([[1, 2], [3, 4]], [3]))
+print(call([[1, 2], [-1, 100]], [1]))  # token 1 is padding: its slots are never read
+def call2(idx1, cv):
+    idx = torch.tensor([[1, 2], [3, 4], [5, 6], [7, 8]], dtype=torch.int32, device=dev)
+    idx1 = torch.tensor(idx1, dtype=torch.int32, device=dev)
+    cv = torch.tensor(cv, dtype=torch.int32, device=dev)
+    try:
+        sdm.sdm_gather(bank, idx, torch.ones(idx.shape, device=dev), chunk=2, chunk_valid=cv, idx1=idx1,
+                       w1=torch.ones(idx1.shape, device=dev))
+        torch.cuda.synchronize()
+        return "ok"
+    except sdm.SdmError as e:
+        return str(e)
+print(call2([[1], [-5], [9], [9]], [1, 2]))
+print(call2([[1], [2], [9], [-5]], [1, 2]))
 '''
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     env = dict(os.environ, SDM_DEBUG_VALIDATE="1")
@@ -216,3 +230,37 @@ print(call([[1, 2], [3, 4]], [3]))
     assert lines[0] == "ok", out.stderr
     assert "outside [0, 100)" in lines[1]
     assert "chunk_valid[0] = 3 outside [0, 2]" in lines[2]
+    assert lines[3] == "ok", lines[3]
+    assert lines[4] == "ok", lines[4]  # operand 1's padding follows chunk_valid too
+    assert "idx1[3, 0] = -5 outside [0, 100)" in lines[5]
+
+
+@pytest.mark.parametrize("per_chunk", [True, False])
+@pytest.mark.parametrize("idt", [torch.int32, torch.int64])
+def test_padding_slots_are_never_read(per_chunk, idt):
+    """Slots of padding tokens set to -1 or far past the bank: the kernel reads no row
+    for them (padding outputs are zeros, stash rows zero), so every result equals
+    the oracle's on the same arrays, bit for bit."""
+    wl = gen.GatherWorkload(name="padding junk", bank_dtype=torch.bfloat16, num_slots=3000, head_dim=128,
+                            tokens=256, chunk=32, valid_low=0, valid_high=32, width0=40, width1=24, idx_dtype=idt,
+                            w_dtype=torch.bfloat16, bank_std=0.5)
+    bank = gen.gather_bank(wl, 61).to(DEV)
+    inp = {k: v.to(DEV) for k, v in gen.gather_inputs(wl, 61).items()}
+    valid = None if per_chunk else 9
+    limit = inp["chunk_valid"].repeat_interleave(wl.chunk) if per_chunk else torch.full((wl.tokens,), 9, device=DEV)
+    pad = torch.arange(wl.tokens, device=DEV) % wl.chunk >= limit
+    assert 0 < int(pad.sum()) < wl.tokens
+    far = torch.iinfo(idt).max
+    for name in ("idx0", "idx1"):
+        junk = torch.where(torch.arange(inp[name].shape[1], device=DEV) % 2 == 0, -1, far).to(idt)
+        inp[name][pad] = junk
+    cv = inp["chunk_valid"] if per_chunk else None
+    out0, st, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, valid=valid, chunk_valid=cv,
+                                idx1=inp["idx1"], w1=inp["w1"])
+    torch.cuda.synchronize()
+    ref0, ref_st, ref1 = oracle.gather(
+        to_np_bank(bank), _np(inp["idx0"]), _np(inp["w0"]), chunk=wl.chunk, valid=valid,
+        chunk_valid=None if cv is None else _np(cv), idx1=_np(inp["idx1"]), w1=_np(inp["w1"]))
+    assert bits_equal(_np(out0), ref0) and bits_equal(_np(out1), ref1)
+    assert bits_equal(to_np_bank(st), ref_st)
+    assert not _np(out0)[pad.cpu().numpy()].any() and not to_np_bank(st)[pad.cpu().numpy()].any()

@@ -137,4 +137,4 @@ except sdm.SdmError as e:
     lines = out.stdout.strip().splitlines()
     assert len(lines) == 2, out.stderr
     assert lines[0] == "ok", lines[0]
-    assert "idx0[71] = 100 outside [0, 100)" in lines[1]
+    assert "idx0[35, 1] = 100 outside [0, 100)" in lines[1]

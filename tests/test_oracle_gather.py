@@ -159,6 +159,43 @@ def test_bad_arguments_are_reported():
         oracle.gather(bank, idx, w, chunk=3)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_padding_slots_are_never_read(bf16):
+    """A padding token reads no row (gather_cuda.py, module docstring: padding positions
+    produce zeros), so any slot value there, in range or not, gives the same results;
+    an out-of-range slot of a live token is still an error, for either operand."""
+    rng = np.random.default_rng(31)
+    bank, idx0, w0 = _rand(rng, 12, 9, 4, 40, bf16)
+    _, idx1, w1 = _rand(rng, 12, 7, 4, 40, bf16)
+    cv = np.array([1, 4, 0], np.int32)  # live tokens: 0, 4..7
+    pad = np.ones(12, bool)
+    pad[[0, 4, 5, 6, 7]] = False
+    ref = oracle.gather(bank, idx0, w0, chunk=4, chunk_valid=cv, idx1=idx1, w1=w1)
+    for junk in (-1, 40, 2**62):
+        j0, j1 = idx0.copy(), idx1.copy()
+        j0[pad] = junk
+        j1[pad] = junk
+        got = oracle.gather(bank, j0, w0, chunk=4, chunk_valid=cv, idx1=j1, w1=w1)
+        for a, b in zip(got, ref):
+            assert bits_equal(a, b)
+        j0, j1 = idx0.copy(), idx1.copy()
+        j0[np.arange(12) % 4 >= 1] = junk  # padding under valid = 1
+        j1[np.arange(12) % 4 >= 1] = junk
+        got = oracle.gather(bank, j0, w0, chunk=4, valid=1, idx1=j1, w1=w1)
+        ref1 = oracle.gather(bank, idx0, w0, chunk=4, valid=1, idx1=idx1, w1=w1)
+        for a, b in zip(got, ref1):
+            assert bits_equal(a, b)
+    bad = idx1.copy()
+    bad[5, 3] = 40  # a live token of chunk 1
+    with pytest.raises(ValueError, match="out of range"):
+        oracle.gather(bank, idx0, w0, chunk=4, chunk_valid=cv, idx1=bad, w1=w1)
+    bad = idx0.copy()
+    bad[1, 0] = -1  # padding under chunk_valid, live when every token is
+    oracle.gather(bank, bad, w0, chunk=4, chunk_valid=cv)
+    with pytest.raises(ValueError, match="out of range"):
+        oracle.gather(bank, bad, w0, chunk=4)
+
+
 # ------------------------------------------------------------ compact stash
 # Page "sparse_delta_memory/cuda/gather_cuda.py": with a position map kpos (one
 # int32 per entry of operand 0: its first position in the chunk's sorted row
