@@ -284,3 +284,43 @@ def test_full_size_configs(name, checked, pin, monkeypatch):
     _say(f"steps {name}: {wl.name}, loop {pin or 'auto'}")
     check_steps(wl, 0, checked, device=DEV, also_single=False)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_full_size_c1_graph_replays(monkeypatch):
+    """Config c1 in the benchmark's default launch path: the whole 64-token sequence as
+    one sdm_decode_steps launch captured in a HIP graph, replayed twice from the same
+    starting bank (restored between replays); sampled streams against the oracle, bit
+    for bit, on every replay."""
+    monkeypatch.delenv("SDM_STEPS_LOOP", raising=False)
+    wl = gen.WORKLOADS["c1"]
+    checked = np.asarray([0, 1, 511, 700, 1023], dtype=np.int64)
+    P = wl.slots_per_stream
+    bank0 = gen.decode_bank(wl, 0, DEV)
+    seq = _sequence(wl, 0, DEV, wl.steps)
+    rows = torch.from_numpy(stream_rows(checked, P)).to(DEV)
+    ref_bank = to_np_bank(bank0[rows])
+    rg = documented_decode_groups(wl.W, wl.R)
+    refs = []
+    for t in range(wl.steps):
+        npin = step_to_numpy({k: v[t] for k, v in seq.items()})
+        refs.append(oracle.decode_step(ref_bank, **sub_inputs(npin, checked, P), groups=rg))
+    bank = bank0.clone()
+    readings = torch.empty(seq["v"].shape, dtype=bank.dtype, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sdm_decode_steps(bank, **seq, readings=readings)
+    sel = torch.from_numpy(checked).to(DEV)
+    for i in range(2):
+        bank.copy_(bank0)
+        readings.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"  replay {i}")
+        for t in range(wl.steps):
+            assert bits_equal(to_np_bank(readings[t][sel]), refs[t]), f"replay {i}, token {t}"
+        assert bits_equal(to_np_bank(bank[rows]), ref_bank), f"replay {i}: bank differs from the oracle"
+    del bank, bank0, graph
+    torch.cuda.empty_cache()

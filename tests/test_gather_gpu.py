@@ -114,17 +114,9 @@ def test_errors_from_python():
     assert o.shape == (0, 4) and s.shape == (0, 2, 4)
 
 
-@pytest.mark.slow
-def test_full_size_c3():
-    """Config c3 at full size: sampled tokens against the oracle bit for bit; every
-    padding token zero and every live stash row equal to its bank row."""
-    wl = gen.WORKLOADS["c3"]
-    _say("c3:", wl.name)
-    bank = gen.gather_bank(wl, 0, DEV)
-    inp = gen.gather_inputs(wl, 0, DEV)
-    out0, stash, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
-                                   idx1=inp["idx1"], w1=inp["w1"])
-    torch.cuda.synchronize()
+def check_c3(wl, bank, inp, out0, stash, out1):
+    """c3's outputs: sampled tokens against the oracle bit for bit; every padding token
+    zero and every live stash row equal to its bank row."""
     T = wl.tokens
     t = torch.arange(T, device=DEV)
     live = (t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]
@@ -155,7 +147,48 @@ def test_full_size_c3():
     assert bits_equal(_np(out0[sample]), ref0)
     assert bits_equal(_np(out1[sample]), ref1)
     assert bits_equal(to_np_bank(stash[sample]), ref_st)
+
+
+@pytest.mark.slow
+def test_full_size_c3():
+    """Config c3 at full size, one eager launch."""
+    wl = gen.WORKLOADS["c3"]
+    _say("c3:", wl.name)
+    bank = gen.gather_bank(wl, 0, DEV)
+    inp = gen.gather_inputs(wl, 0, DEV)
+    out0, stash, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+                                   idx1=inp["idx1"], w1=inp["w1"])
+    torch.cuda.synchronize()
+    check_c3(wl, bank, inp, out0, stash, out1)
     del bank, stash
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_full_size_c3_graph_replays():
+    """Config c3 at full size in the benchmark's launch path: the launch captured in a
+    HIP graph, outputs cleared between replays, every replay checked."""
+    wl = gen.WORKLOADS["c3"]
+    bank = gen.gather_bank(wl, 0, DEV)
+    inp = gen.gather_inputs(wl, 0, DEV)
+    out0 = torch.empty((wl.tokens, wl.head_dim), dtype=torch.float32, device=DEV)
+    out1 = torch.empty_like(out0)
+    stash = torch.empty((wl.tokens, wl.width0, wl.head_dim), dtype=bank.dtype, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"], idx1=inp["idx1"],
+                   w1=inp["w1"], out0=out0, stash=stash, out1=out1)
+    for i in range(2):
+        out0.fill_(float("nan"))
+        out1.fill_(float("nan"))
+        stash.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"  replay {i}")
+        check_c3(wl, bank, inp, out0, stash, out1)
+    del bank, stash, graph
     torch.cuda.empty_cache()
 
 
