@@ -287,14 +287,19 @@ def test_full_size_configs(name, checked, pin, monkeypatch):
 
 
 @pytest.mark.slow
-def test_full_size_c1_graph_replays(monkeypatch):
-    """Config c1 in the benchmark's default launch path: the whole 64-token sequence as
+@pytest.mark.parametrize("name,checked", [
+    ("c1", [0, 1, 511, 700, 1023]),
+    ("c2", [0, 17, 2048, 4095]),
+    ("c4", [0, 3, 256, 511]),
+])
+def test_full_size_graph_replays(name, checked, monkeypatch):
+    """A full-size workload in the benchmark's launch path: its whole token sequence as
     one sdm_decode_steps launch captured in a HIP graph, replayed twice from the same
     starting bank (restored between replays); sampled streams against the oracle, bit
     for bit, on every replay."""
     monkeypatch.delenv("SDM_STEPS_LOOP", raising=False)
-    wl = gen.WORKLOADS["c1"]
-    checked = np.asarray([0, 1, 511, 700, 1023], dtype=np.int64)
+    wl = gen.WORKLOADS[name]
+    checked = np.asarray(checked, dtype=np.int64)
     P = wl.slots_per_stream
     bank0 = gen.decode_bank(wl, 0, DEV)
     seq = _sequence(wl, 0, DEV, wl.steps)
