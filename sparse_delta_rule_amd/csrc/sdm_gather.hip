@@ -91,9 +91,20 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const int pair = tid / p.lpr;
     const int g = pair / NOPS;               // token within the block
     const int op = pair - g * NOPS;          // operand
-    const int64_t t_first = int64_t(blockIdx.x) * tpb;
+    // Workgroups are handed to the XCDs in turn (workgroup i to XCD i mod 8): give
+    // XCD x a contiguous share of the (token block, slice) pairs, so chunk positions
+    // (live heads, padding tails) mix evenly over the XCDs.
+    int64_t tblock, slice;
+    {
+        const int64_t n = int64_t(gridDim.x) * gridDim.y, i = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+        const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;
+        const int64_t j = x * q + (x < r ? x : r) + k;
+        tblock = j % gridDim.x;
+        slice = j / gridDim.x;
+    }
+    const int64_t t_first = tblock * tpb;
     const int64_t t = t_first + g;
-    const int vi = int(blockIdx.y) * p.lpr + lane;
+    const int vi = int(slice) * p.lpr + lane;
     const bool lane_on = t < p.tokens && vi < p.vpr;
     const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
 
