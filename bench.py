@@ -470,7 +470,7 @@ def main(argv=None):
         return ingest_profile(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+        print(f"bench.py: the benchmark measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world}); a step is one GPU's share of streams or tokens, which needs no exchange.",
               file=sys.stderr, flush=True)
         return 2
