@@ -139,73 +139,140 @@ def _run_steps(torch, args, launch_one, K):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline_decode(torch, wl, bank, seq, target_s, cfg_name):
-    """Time the oracle (single thread) on a subset of streams over the whole sequence."""
+def host_threads() -> int:
+    """Host threads for the all-cores oracle run: the process's CPUs, at most the
+    OMP_NUM_THREADS share when that is set, and at most 16."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, 16))
+
+
+def _bank_np(torch, t):
     import numpy as np
-    import oracle
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16).copy() if t.dtype == torch.bfloat16 else t.float().numpy().copy()
+
+
+def decode_groups(torch, wl, bank, seq, n, groups):
+    """Streams [0, n) of a decode workload as ``groups`` contiguous stream ranges, each
+    with its own bank rows and inputs (slots renumbered into its rows): what one
+    oracle thread steps through the whole sequence."""
     P = wl.slots_per_stream
-
-    def to_np(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
-
-    def subset(n):
-        streams = torch.arange(n, device=bank.device)
-        rows = (streams[:, None] * P + torch.arange(P, device=bank.device)[None, :]).ravel()
-        b = to_np(bank[rows]).copy()
+    bounds = [n * g // groups for g in range(groups + 1)]
+    out = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        if a == b:
+            continue
+        rows = (torch.arange(a, b, device=bank.device)[:, None] * P
+                + torch.arange(P, device=bank.device)[None, :]).ravel()
         steps = []
         for inp in seq:
             d = {}
             for k, v in inp.items():
-                v = v[:n].detach().cpu()
-                d[k] = v.to(torch.int64).numpy() if k in ("k_idx", "q_idx") else v.float().numpy()
+                v = v[a:b].detach().cpu()
+                d[k] = (v.to(torch.int64) - a * P).numpy() if k in ("k_idx", "q_idx") else v.float().numpy()
             steps.append(d)
-        return b, steps
+        out.append((_bank_np(torch, bank[rows]), steps))
+    return out
 
-    # calibrate on 4 streams x 2 steps, then size the sample for ~target_s of work
-    b, steps = subset(min(4, wl.streams))
+
+def run_decode_groups(groups):
+    """Step every group through its sequence, one thread per group (the oracle's C
+    calls release the GIL). Returns each group's readings per step."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+
+    def one(grp):
+        b, steps = grp
+        return [oracle.decode_step(b, **inp) for inp in steps]
+
+    with ThreadPoolExecutor(max_workers=max(1, len(groups))) as ex:
+        return list(ex.map(one, groups))
+
+
+def cpu_baseline_decode(torch, wl, bank, seq, target_s, cfg_name):
+    """Time the oracle on a subset of streams over the whole sequence: one thread, and
+    one thread per host core over contiguous stream groups."""
+    # calibrate on 32 streams x 2 steps (enough work that fixed call costs do not
+    # dominate), then size the sample for ~target_s of work
+    m = min(32, wl.streams)
+    (b, steps), = decode_groups(torch, wl, bank, seq[:2], m, 1)
     t0 = time.perf_counter()
-    for inp in steps[:2]:
-        oracle.decode_step(b, **inp)
-    per = (time.perf_counter() - t0) / (2 * min(4, wl.streams))
+    run_decode_groups([(b, steps)])
+    per = (time.perf_counter() - t0) / (2 * m)
     n = int(max(1, min(wl.streams, target_s / max(per * len(seq), 1e-9))))
-    b, steps = subset(n)
+    grp = decode_groups(torch, wl, bank, seq, n, 1)
     t0 = time.perf_counter()
-    for inp in steps:
-        oracle.decode_step(b, **inp)
+    run_decode_groups(grp)
     dt = time.perf_counter() - t0
-    return {"value": n * len(steps) / dt, "unit": "stream-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {wl.streams} streams x all {len(steps)} steps of {cfg_name} "
-                      f"(single-threaded C oracle, {dt:.1f} s)"}
+    cores = host_threads()
+    n_all = int(max(1, min(wl.streams, n * cores)))
+    grp = decode_groups(torch, wl, bank, seq, n_all, cores)
+    t0 = time.perf_counter()
+    run_decode_groups(grp)
+    dt_all = time.perf_counter() - t0
+    return {"value": n * len(seq) / dt, "unit": "stream-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.streams} streams x all {len(seq)} steps of {cfg_name} "
+                      f"(single-threaded C oracle, {dt:.1f} s)",
+            "all_cores": {"value": n_all * len(seq) / dt_all, "unit": "stream-steps/s", "cores": len(grp),
+                          "sample": f"{n_all} of {wl.streams} streams x all {len(seq)} steps, one thread per "
+                                    f"group of streams ({dt_all:.1f} s)"}}
+
+
+def gather_ranges(torch, wl, bank, inp, n, groups):
+    """Tokens [0, n) of the gather workload (n a multiple of the chunk) as ``groups``
+    chunk-aligned token ranges over one shared sub-bank of the rows they touch."""
+    sel = torch.arange(n, device=bank.device)
+    i0, i1 = inp["idx0"][sel].long(), inp["idx1"][sel].long()
+    uniq, inv = torch.unique(torch.cat([i0.ravel(), i1.ravel()]), return_inverse=True)
+    sub = _bank_np(torch, bank[uniq])
+    a0 = inv[:i0.numel()].view_as(i0).cpu().numpy()
+    a1 = inv[i0.numel():].view_as(i1).cpu().numpy()
+    w0 = inp["w0"][sel].float().cpu().numpy()
+    w1 = inp["w1"][sel].float().cpu().numpy()
+    cv = inp["chunk_valid"][: n // wl.chunk].cpu().numpy()
+    chunks = n // wl.chunk
+    bounds = [chunks * g // groups * wl.chunk for g in range(groups + 1)]
+    return sub, [(a0[a:b], w0[a:b], a1[a:b], w1[a:b], cv[a // wl.chunk:b // wl.chunk])
+                 for a, b in zip(bounds[:-1], bounds[1:]) if a < b]
+
+
+def run_gather_ranges(wl, sub, ranges):
+    """The oracle's gather over each token range, one thread per range. Returns each
+    range's (out0, stash, out1)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+
+    def one(r):
+        a0, w0, a1, w1, cv = r
+        return oracle.gather(sub, a0, w0, chunk=wl.chunk, chunk_valid=cv, idx1=a1, w1=w1)
+
+    with ThreadPoolExecutor(max_workers=max(1, len(ranges))) as ex:
+        return list(ex.map(one, ranges))
 
 
 def cpu_baseline_gather(torch, wl, bank, inp, live, target_s, cfg_name):
-    import numpy as np
-    import oracle
-
-    def to_np(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.float().numpy()
-
-    def run(n):
-        sel = torch.arange(n, device=bank.device)
-        i0, i1 = inp["idx0"][sel].long(), inp["idx1"][sel].long()
-        uniq, inv = torch.unique(torch.cat([i0.ravel(), i1.ravel()]), return_inverse=True)
-        sub = to_np(bank[uniq])
-        a0 = inv[:i0.numel()].view_as(i0).cpu().numpy()
-        a1 = inv[i0.numel():].view_as(i1).cpu().numpy()
-        w0 = inp["w0"][sel].float().cpu().numpy()
-        w1 = inp["w1"][sel].float().cpu().numpy()
-        cv = inp["chunk_valid"][: n // wl.chunk].cpu().numpy()
+    """Time the oracle on the first tokens of the launch: one thread, and one thread per
+    host core over chunk-aligned token ranges."""
+    def timed(n, groups):
+        sub, ranges = gather_ranges(torch, wl, bank, inp, n, groups)
         t0 = time.perf_counter()
-        oracle.gather(sub, a0, w0, chunk=wl.chunk, chunk_valid=cv, idx1=a1, w1=w1)
-        return time.perf_counter() - t0
+        run_gather_ranges(wl, sub, ranges)
+        return time.perf_counter() - t0, len(ranges)
 
-    per = run(wl.chunk * 4) / (wl.chunk * 4)
+    per = timed(wl.chunk * 4, 1)[0] / (wl.chunk * 4)
     n = int(max(wl.chunk, min(wl.tokens, target_s / max(per, 1e-9))) // wl.chunk * wl.chunk)
-    dt = run(n)
+    dt, _ = timed(n, 1)
+    cores = host_threads()
+    n_all = int(max(wl.chunk, min(wl.tokens, n * cores)) // wl.chunk * wl.chunk)
+    dt_all, used = timed(n_all, cores)
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {wl.tokens} tokens of {cfg_name} (single-threaded C oracle, {dt:.1f} s)"}
+            "sample": f"first {n} of {wl.tokens} tokens of {cfg_name} (single-threaded C oracle, {dt:.1f} s)",
+            "all_cores": {"value": n_all / dt_all, "unit": "tokens/s", "cores": used,
+                          "sample": f"first {n_all} of {wl.tokens} tokens, one thread per chunk-aligned "
+                                    f"range ({dt_all:.1f} s)"}}
 
 
 # ------------------------------------------------------------------ workloads

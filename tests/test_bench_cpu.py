@@ -123,3 +123,50 @@ def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     (src / "k.hip").write_text("int f(int x) { return x + 2; }\n")
     assert bench.kernel_source_hash() != h0
+
+
+# ------------------------------------------------------------ CPU baseline legs
+def test_host_threads_is_bounded(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.host_threads() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert 1 <= bench.host_threads() <= 16
+
+
+def test_decode_groups_give_the_whole_runs_bits():
+    """The all-cores oracle run steps contiguous stream groups on their own bank rows
+    (slots renumbered): its readings and rows equal one run over all the streams."""
+    import numpy as np
+    import torch
+    import gen
+    wl = gen.WORKLOADS["c1"].replace(streams=11, slots_per_stream=64, steps=3)
+    bank = gen.decode_bank(wl, 0)
+    seq = [gen.decode_step_inputs(wl, 0, t) for t in range(wl.steps)]
+    whole = bench.decode_groups(torch, wl, bank, seq, 11, 1)
+    split = bench.decode_groups(torch, wl, bank, seq, 11, 4)
+    assert len(split) == 4
+    r_whole = bench.run_decode_groups(whole)[0]
+    r_split = bench.run_decode_groups(split)
+    for t in range(wl.steps):
+        got = np.concatenate([r[t] for r in r_split])
+        assert np.array_equal(got.view(np.uint16), r_whole[t].view(np.uint16)), f"step {t}"
+    banks = np.concatenate([g[0] for g in split])
+    assert np.array_equal(banks.view(np.uint16), whole[0][0].view(np.uint16))
+
+
+def test_gather_ranges_give_the_whole_runs_bits():
+    import numpy as np
+    import torch
+    import gen
+    wl = gen.WORKLOADS["c3"].replace(num_slots=3000, tokens=7 * 16, chunk=16, width0=9, width1=5, valid_low=2,
+                                     valid_high=16)
+    bank = gen.gather_bank(wl, 2)
+    inp = gen.gather_inputs(wl, 2)
+    sub, whole = bench.gather_ranges(torch, wl, bank, inp, wl.tokens, 1)
+    sub2, split = bench.gather_ranges(torch, wl, bank, inp, wl.tokens, 3)
+    assert len(split) == 3 and np.array_equal(sub, sub2)
+    (w0, ws, w1), = bench.run_gather_ranges(wl, sub, whole)
+    parts = bench.run_gather_ranges(wl, sub, split)
+    assert np.array_equal(np.concatenate([p[0] for p in parts]).view(np.uint32), w0.view(np.uint32))
+    assert np.array_equal(np.concatenate([p[1] for p in parts]).view(np.uint16), ws.view(np.uint16))
+    assert np.array_equal(np.concatenate([p[2] for p in parts]).view(np.uint32), w1.view(np.uint32))
