@@ -8,6 +8,8 @@ metadata items per thread, the multi-token loop) meet in combinations no list
 names. Every comparison is bit for bit, as in the other parity tests.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,9 @@ from tests.test_gather_compact_gpu import run_compact
 from tests.test_gather_gpu import run_case
 
 pytestmark = pytest.mark.gpu
+
+# Cases per sweep; SDM_SWEEP_CASES=<n> runs a longer sweep (same seeds, more of them).
+N_CASES = int(os.environ.get("SDM_SWEEP_CASES", "0")) or None
 
 HEAD_DIMS = [1, 2, 3, 5, 8, 16, 31, 64, 100, 101, 127, 128, 129, 200, 255, 256, 300, 512, 700]
 WIDTHS = [1, 2, 3, 4, 5, 7, 8, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256]
@@ -40,7 +45,7 @@ def _decode_case(i):
 
 
 @pytest.mark.parametrize("loop", ["auto", "compact", "wide"])
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(N_CASES or 40))
 def test_random_decode_shapes(i, loop, monkeypatch):
     """A multi-token launch on a random shape equals the oracle stepped token by token
     and equals one single-token launch per token."""
@@ -64,7 +69,7 @@ def _gather_case(i):
         w_dtype=_pick(rng, [torch.float32, torch.bfloat16]), bank_std=0.5)
 
 
-@pytest.mark.parametrize("i", range(64))
+@pytest.mark.parametrize("i", range(N_CASES or 64))
 def test_random_gather_shapes(i):
     """The gather (with and without the stash, per-chunk or scalar valid) and the
     compact-stash gather on a random shape equal the oracle."""
