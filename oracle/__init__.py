@@ -9,9 +9,12 @@ arrays into it.
 Parity pins (the tests under ``tests/`` named ``test_oracle_*``) tie every
 function here to the method's definitions: hand-worked dyadic cases, closed
 forms, identities, read-after-write, a float64 brute force with an error bound,
-and a library routine for the bfloat16 rounding. Parity of the decode's
-float32 summation order is pinned only by that error bound, since the method
-fixes no order (several results are correct).
+and a library routine for the bfloat16 rounding. The decode's float32 choices
+that the method leaves open (the summation order, k_val * d rounded before the
+products, delta_v's two roundings, the fused update) are pinned by worked
+float32 values that the other plausible choices miss, on top of the bound.
+tests/test_oracle_mutants.py runs the pins against broken copies of the C
+source and requires each copy to fail one of them.
 
 Bank arrays are float32, or uint16 holding bfloat16 bits.
 """
@@ -27,6 +30,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sdm_oracle.c")
 _LIB = os.path.join(_HERE, "libsdm_oracle.so")
+# SDM_ORACLE_LIBRARY names another build of sdm_oracle.c to load instead (used by
+# the test that runs the pins against deliberately broken copies); it is loaded
+# as it is, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("SDM_ORACLE_LIBRARY", "")
 
 _lib = None
 
@@ -48,9 +55,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int
     lib.sdm_oracle_decode_step.argtypes = [P, i32, i64, i64, i64, i32, i32, i32, i32,

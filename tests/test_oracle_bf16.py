@@ -107,3 +107,20 @@ def test_double_rounding_differs_from_two_step():
 @pytest.mark.parametrize("b", [0, 1, 0x3f80, 0x7f7f, 0x8001, 0xc2f7])
 def test_widening_is_exact(b):
     assert oracle.bf16_to_float(b) == float(np.array([b << 16], np.uint32).view(np.float32)[0])
+
+
+@pytest.mark.parametrize("bits", [0x7f800001, 0xff800001, 0x7f80ffff, 0x7fa00000])
+def test_nan_with_low_payload_stays_nan_in_the_decode(bits):
+    """A float32 NaN whose payload lies only in the low 16 bits (or a signalling NaN)
+    truncates to the bits of an infinity; the rounding must still give a NaN (the
+    reading "NaN stays NaN"). Passed as raw float32 bits through the decode on a
+    bfloat16 bank, where v is rounded to the bank dtype: the written row and the
+    reading of it are NaNs, not infinities. (A Python float would quiet the NaN on
+    its way in, which is why this goes through an array.)"""
+    bank = np.array([[0x3f80]], np.uint16)  # one slot, hd 1: 1.0
+    v = np.array([[bits]], np.uint32).view(np.float32)
+    readings = oracle.decode_step(bank, np.array([[0]]), np.array([[1.0]], np.float32), v,
+                                  np.array([[1.0]], np.float32), np.array([[0.0]], np.float32), np.array([[0]]),
+                                  np.array([[1.0]], np.float32))
+    for b in (int(bank[0, 0]), int(readings[0, 0])):
+        assert (b & 0x7f80) == 0x7f80 and (b & 0x007f) != 0, hex(b)
