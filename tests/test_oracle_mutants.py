@@ -70,6 +70,14 @@ MUTANTS = {
     "gather: compact stash one position on": [
         ("memcpy((unsigned char*)stash + (size_t)((k * crow + p) * hd * es),",
          "memcpy((unsigned char*)stash + (size_t)((k * crow + (p + 1) % crow) * hd * es),")],
+    "gather: padding outputs -0": [("for (int64_t c = 0; c < hd; ++c) out[t * hd + c] = 0.0f;",
+                                    "for (int64_t c = 0; c < hd; ++c) out[t * hd + c] = -0.0f;")],
+    "gather: padding stash rows not zero": [("else memset(row, 0, (size_t)(hd * es));",
+                                             "else memset(row, 0xff, (size_t)(hd * es));")],
+    "compact stash: padding tokens stored too": [
+        ("            if (!token_live(t, chunk, valid, chunk_valid)) continue;\n            for (int n = 0; n < width0;",
+         "            for (int n = 0; n < width0;")],
+    "brute force: decode decay dropped": [("d[w] = exp((double)g[s * G + (G == 1 ? 0 : w)]);", "d[w] = 1.0;")],
     "brute force: decode delta sign flipped": [("dv[c] = b * (vc - retrieved);\n            dvmag",
                                                 "dv[c] = b * (retrieved - vc);\n            dvmag")],
     "brute force: gather weight dropped": [
