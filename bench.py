@@ -16,7 +16,9 @@ the kernels run on.
 
 Prints one JSON line: stream-steps/s (tokens/s for the gather), the achieved
 bank-row bandwidth against the MI355X's 8 TB/s HBM peak, and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload (one thread, and all host
+cores). A decode run with the default entry also times the same tokens as one
+sdm_decode_step launch each, reported under "single_token".
 """
 
 from __future__ import annotations
@@ -294,7 +296,6 @@ def bench_decode(torch, args, cfg_name, wl):
         if K % T:
             raise SystemExit(f"bench.py: --steps must be a multiple of the {T}-token sequence with --entry steps")
         stacked = {k: torch.stack([d[k] for d in seq]) for k in seq[0]}
-        del seq
         readings = torch.empty((T, wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev)
 
         def launch_one(i):
@@ -320,8 +321,22 @@ def bench_decode(torch, args, cfg_name, wl):
               "entry": "sdm_decode_steps" if args.entry == "steps" else "sdm_decode_step",
               "tokens_per_launch": per_launch, "launch": args.launch, "seed": args.seed}
     value = wl.streams * K / (ms * 1e-3)
+    single = None
+    if args.entry == "steps":
+        # the same tokens, one sdm_decode_step launch each (the bank keeps changing)
+        del stacked, readings
+        outs = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
+
+        def launch_single(i):
+            sdm_decode_step(bank, **seq[i % T], readings=outs[i % T])
+
+        ms1 = _run_steps(torch, args, launch_single, T)
+        single = {"entry": "sdm_decode_step", "tokens_per_launch": 1, "steps": T, "ms_per_step": ms1 / T,
+                  "value": wl.streams * T / (ms1 * 1e-3), "unit": "stream-steps/s",
+                  "achieved": row_bytes_step / (ms1 / T * 1e-3) / 1e9, "frac":
+                  row_bytes_step / (ms1 / T * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     return dict(value=value, unit="stream-steps/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=launch_bytes, cpu=cpu, tokens_per_s=value)
+                row_bytes=launch_bytes, cpu=cpu, tokens_per_s=value, single=single)
 
 
 def bench_gather(torch, args, cfg_name, wl):
@@ -578,6 +593,8 @@ def main(argv=None):
         "tokens_per_s": r["tokens_per_s"],
         "row_gbps": r["gbps"],
     }
+    if r.get("single"):
+        out["single_token"] = r["single"]
     print(json.dumps(out), flush=True)
     return 0
 
