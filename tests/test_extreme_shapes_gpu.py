@@ -1,0 +1,55 @@
+"""Parity at the far ends of the shapes: very long rows (many column slices), the
+widest widths on the narrowest rows, one chunk spanning every token and chunks of
+one token. Bit for bit against the oracle, as the other parity tests."""
+
+import pytest
+import torch
+
+import gen
+from tests.test_decode_steps_gpu import check_steps
+from tests.test_gather_compact_gpu import run_compact
+from tests.test_gather_gpu import run_case
+
+pytestmark = pytest.mark.gpu
+
+DECODE = [
+    # name, bank dtype, streams, slots/stream, hd, W, R, G, steps
+    ("f32 hd 4096 (32 slices of 512 B)", torch.float32, 6, 64, 4096, 9, 7, 9, 3),
+    ("bf16 hd 8192 (32 slices)", torch.bfloat16, 4, 40, 8192, 5, 12, 1, 2),
+    ("f32 hd 1 W = R = 256", torch.float32, 5, 300, 1, 256, 256, 256, 3),
+    ("bf16 hd 2 W = R = 256", torch.bfloat16, 3, 256, 2, 256, 256, 1, 2),
+    ("bf16 hd 4095 odd long", torch.bfloat16, 3, 20, 4095, 3, 3, 3, 2),
+    ("f32 many streams, one slot each", torch.float32, 3000, 1, 16, 1, 1, 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_extremes(case):
+    name, dt, S, P, hd, W, R, G, T = case
+    wl = gen.DecodeWorkload(name=name, bank_dtype=dt, streams=S, slots_per_stream=P, head_dim=hd, W=W, R=R, G=G,
+                            steps=T, idx_dtype=torch.int64, weights="normal_sqrtw", beta="sigmoid", g_low=-0.2,
+                            bank_std=0.5)
+    print(name, flush=True)
+    check_steps(wl, 61, list(range(S)))
+
+
+GATHER = [
+    # name, bank dtype, slots, hd, tokens, chunk, width0, width1
+    ("bf16 hd 8192 (16 slices)", torch.bfloat16, 500, 8192, 12, 4, 6, 3),
+    ("f32 hd 4096", torch.float32, 300, 4096, 10, 5, 4, 0),
+    ("one chunk of every token", torch.bfloat16, 3000, 128, 200, 200, 32, 32),
+    ("chunks of one token", torch.bfloat16, 3000, 128, 150, 1, 16, 8),
+    ("hd 1, widths 256", torch.float32, 1000, 1, 40, 8, 256, 256),
+]
+
+
+@pytest.mark.parametrize("case", GATHER, ids=[c[0] for c in GATHER])
+def test_gather_extremes(case):
+    name, dt, slots, hd, T, chunk, W0, W1 = case
+    wl = gen.GatherWorkload(name=name, bank_dtype=dt, num_slots=slots, head_dim=hd, tokens=T, chunk=chunk,
+                            valid_low=0, valid_high=chunk, width0=W0, width1=W1, idx_dtype=torch.int32,
+                            w_dtype=torch.bfloat16, bank_std=0.5)
+    print(name, flush=True)
+    run_case(wl, 62, per_chunk=True)
+    run_case(wl, 62, per_chunk=False, valid=max(1, chunk - 1))
+    run_compact(wl, 62)
