@@ -2,7 +2,8 @@
 
     python -m sparse_delta_rule_amd.build
 
-The library is built in-tree, next to this file, from csrc/*.hip.
+The library is built in-tree, next to this file, from csrc/*.hip; then the
+plain C example caller in examples/ is compiled against it.
 """
 
 from __future__ import annotations
@@ -34,6 +35,31 @@ def sources() -> list:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+EXAMPLE_SRC = os.path.join(HERE, "examples", "sdm_example.c")
+EXAMPLE = os.path.join(HERE, "examples", "sdm_example")
+
+
+def build_example(verbose: bool = False) -> str:
+    """The plain C example caller (examples/sdm_example.c), linked against the
+    in-tree libsdm.so (found next to the examples folder at run time) and the HIP
+    runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = os.environ.get("CC", "gcc")
+    tmp = EXAMPLE + ".tmp"
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), "-o", tmp, EXAMPLE_SRC, "-L", HERE, "-lsdm",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/..",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"{cc} failed ({r.returncode}) building {EXAMPLE}")
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
@@ -45,6 +71,7 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed ({r.returncode}) building {LIB}")
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
 
 
