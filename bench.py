@@ -8,9 +8,10 @@ decode step), or one sdm_gather launch over every token (--config c3). Inputs
 are seeded and synthetic (gen/), generated on the GPU and resident in HBM
 before the timed region; the decode runs the workload's token sequence, the
 bank changing from token to token as the method intends. By default a decode
-launch is one sdm_decode_steps call over the whole sequence (K must be a
-multiple of its length); ``--entry step`` launches sdm_decode_step once per
-token instead. The timed launches run as one HIP-graph replay (``--launch
+launch is one sdm_decode_steps call over the whole sequence, and K defaults to
+four passes of it, timed back to back (any K is accepted: whole passes, then
+the sequence's first K mod T tokens in one more launch); ``--entry step``
+launches sdm_decode_step once per token instead (K defaults to one pass). The timed launches run as one HIP-graph replay (``--launch
 eager`` launches from Python instead) bracketed by HIP events on the stream
 the kernels run on.
 
@@ -290,18 +291,26 @@ def bench_decode(torch, args, cfg_name, wl):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_decode(torch, wl, bank, seq, args.cpu_seconds, cfg_name)
-    K = args.steps if args.steps is not None else T
+    # default: four passes of the token sequence (the multi-token entry point), or
+    # the sequence once (one launch per token); any K >= 1 is accepted
+    K = args.steps if args.steps is not None else (4 * T if args.entry == "steps" else T)
+    if K < 1:
+        raise SystemExit("bench.py: --steps must be at least 1")
     row_bytes_step = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
     if args.entry == "steps":
-        if K % T:
-            raise SystemExit(f"bench.py: --steps must be a multiple of the {T}-token sequence with --entry steps")
         stacked = {k: torch.stack([d[k] for d in seq]) for k in seq[0]}
         readings = torch.empty((T, wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev)
+        # K tokens per stream: whole passes of the sequence, then its first K mod T tokens
+        plan = [T] * (K // T) + ([K % T] if K % T else [])
+        part = {k: v[:K % T].contiguous() for k, v in stacked.items()} if K % T else None
 
         def launch_one(i):
-            sdm_decode_steps(bank, **stacked, readings=readings)
+            if plan[i % len(plan)] == T:
+                sdm_decode_steps(bank, **stacked, readings=readings)
+            else:
+                sdm_decode_steps(bank, **part, readings=readings[:K % T])
 
-        launches, per_launch = K // T, T
+        launches, per_launch = len(plan), plan[0]
     else:
         readings = [torch.empty((wl.streams, wl.head_dim), dtype=wl.bank_dtype, device=dev) for _ in seq]
 
@@ -313,7 +322,7 @@ def bench_decode(torch, args, cfg_name, wl):
     ms = _run_steps(torch, args, launch_one, launches)
     ms_step = ms / K
     launch_bytes = row_bytes_step * per_launch
-    gbps = launch_bytes / (ms / launches * 1e-3) / 1e9
+    gbps = row_bytes_step * K / (ms * 1e-3) / 1e9  # = bytes per launch / mean launch time
     config = {"workload": f"{cfg_name}: {wl.name}", "streams": wl.streams, "slots": wl.num_slots,
               "head_dim": wl.head_dim, "W": wl.W, "R": wl.R, "G": wl.G,
               "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "index_dtype":
