@@ -1,7 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the sparse-delta-memory hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--entry steps|step]
+    python bench.py [--steps K] [--warmup W] [--config c2|c1|c3|c4|c0] [--entry steps|step]
+
+The default workload is c2: 4096 streams over a 16 GiB bfloat16 bank, W = R = 64
+rows of 256 bytes, a gate per write, 32 tokens per stream.
 
 A step is one decode token for every stream of the workload (one pass of the
 decode step), or one sdm_gather launch over every token (--config c3). Inputs
@@ -19,7 +22,10 @@ Prints one JSON line: stream-steps/s (tokens/s for the gather), the achieved
 bank-row bandwidth against the MI355X's 8 TB/s HBM peak, and the CPU oracle
 timed on a bounded sample of the same workload (one thread, and all host
 cores). A decode run with the default entry also times the same tokens as one
-sdm_decode_step launch each, reported under "single_token".
+sdm_decode_step launch each, reported under "single_token". The line also gives
+the rate of a plain streaming device copy measured in the same run
+(roofline.copy_gbps) and each rate as a fraction of it (copy_frac), and the
+host the CPU baseline ran on (cpu_baseline.host).
 """
 
 from __future__ import annotations
@@ -37,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "stream-steps/sec + achieved HBM GB/s (bank row bytes) on one MI355X"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+STORAGE_DTYPE = {"torch.bfloat16": "bf16", "torch.float32": "f32"}
 
 
 def kernel_source_hash() -> str:
@@ -70,9 +77,16 @@ def kernel_pattern(kind: str) -> str:
 KERNEL_PATTERN = {"gather": "sdm_gather_kernel", "steps": "sdm_decode_steps", "step": "sdm_decode_kernel"}
 
 
-def stored_traffic(config: str, kind: str):
-    """(HBM bytes per launch, kernel name) measured by rocprofv3 for this config and launch
-    kind, if taken on the current kernel sources (profiles/traffic.json), else (None, None)."""
+def stored_traffic(config: str, kind: str, tokens_per_launch: int = 1, live_tokens=None):
+    """(HBM bytes, kernel name) that rocprofv3 measured for one launch of this shape
+    (profiles/traffic.json), or (None, None) when no figure applies.
+
+    A figure applies only while the kernel sources are the ones it was taken on. A
+    decode entry holds the bytes of a launch of ``tokens_per_launch`` tokens and is
+    scaled to the asked launch's token count (each token of a launch moves the same
+    rows); a multi-token figure does not stand for a single-token launch, which runs
+    another kernel. A gather entry applies only to a launch with the same live-token
+    count."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None, None
@@ -81,7 +95,16 @@ def stored_traffic(config: str, kind: str):
     entry = data.get(f"{config}/{kind}")
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None, None
-    return entry.get("bytes_per_launch"), entry.get("kernel")
+    stored_tokens = entry.get("tokens_per_launch")
+    if not stored_tokens or not entry.get("bytes_per_launch"):
+        return None, None
+    if kind.startswith("gather"):
+        if live_tokens is None or entry.get("live_tokens") != live_tokens:
+            return None, None
+        return entry["bytes_per_launch"], entry.get("kernel")
+    if (stored_tokens == 1) != (tokens_per_launch == 1):
+        return None, None
+    return entry["bytes_per_launch"] / stored_tokens * tokens_per_launch, entry.get("kernel")
 
 
 def parse_args(argv=None):
@@ -89,7 +112,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's sequence)")
     p.add_argument("--warmup", type=int, default=8)
-    p.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--config", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--launch", default="graph", choices=["graph", "eager"])
     p.add_argument("--entry", default="steps", choices=["steps", "step"],
@@ -142,14 +165,61 @@ def _run_steps(torch, args, launch_one, K):
 
 
 # ------------------------------------------------------------------ CPU baseline
+THREAD_CAP = 16
+THREAD_CAP_REASON = ("one GPU's share of the host: the GPU box gives a one-GPU job 16 CPUs "
+                     "(OMP_NUM_THREADS=16 there), whatever the machine's core count")
+
+
 def host_threads() -> int:
     """Host threads for the all-cores oracle run: the process's CPUs, at most the
-    OMP_NUM_THREADS share when that is set, and at most 16."""
+    OMP_NUM_THREADS share when that is set, and at most THREAD_CAP."""
     n = len(os.sched_getaffinity(0))
     omp = os.environ.get("OMP_NUM_THREADS", "")
     if omp.isdigit() and int(omp) > 0:
         n = min(n, int(omp))
-    return max(1, min(n, 16))
+    return max(1, min(n, THREAD_CAP))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name as lscpu reports it (else from /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.split(":", 1)[0].strip() == "Model name":
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_record() -> dict:
+    """What the CPU baseline ran on: core counts, model and the thread cap."""
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "model": cpu_model(),
+            "thread_cap": THREAD_CAP, "thread_cap_reason": THREAD_CAP_REASON,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+class pinned_to_one_cpu:
+    """Pin the calling thread (and the threads it starts meanwhile, which inherit its
+    mask) to one CPU of the process's set, as ``taskset -c`` would; restore on exit."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.cpu = min(self.saved)
+        os.sched_setaffinity(0, {self.cpu})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+        return False
 
 
 def _bank_np(torch, t):
@@ -160,25 +230,38 @@ def _bank_np(torch, t):
 
 def decode_groups(torch, wl, bank, seq, n, groups):
     """Streams [0, n) of a decode workload as ``groups`` contiguous stream ranges, each
-    with its own bank rows and inputs (slots renumbered into its rows): what one
-    oracle thread steps through the whole sequence."""
-    P = wl.slots_per_stream
+    with the bank rows its sequence touches (its private rows that some step writes or
+    reads, in slot order) and its inputs with the slots renumbered into those rows:
+    what one oracle thread steps through the whole sequence. Rows no step touches
+    cannot change any reading or touched row, so they are left out."""
     bounds = [n * g // groups for g in range(groups + 1)]
     out = []
     for a, b in zip(bounds[:-1], bounds[1:]):
         if a == b:
             continue
-        rows = (torch.arange(a, b, device=bank.device)[:, None] * P
-                + torch.arange(P, device=bank.device)[None, :]).ravel()
+        used = torch.unique(torch.cat([inp[k][a:b].reshape(-1).to(torch.int64)
+                                       for inp in seq for k in ("k_idx", "q_idx")]))
         steps = []
         for inp in seq:
             d = {}
             for k, v in inp.items():
-                v = v[a:b].detach().cpu()
-                d[k] = (v.to(torch.int64) - a * P).numpy() if k in ("k_idx", "q_idx") else v.float().numpy()
+                v = v[a:b]
+                if k in ("k_idx", "q_idx"):
+                    d[k] = torch.searchsorted(used, v.to(torch.int64).contiguous()).cpu().numpy()
+                else:
+                    d[k] = v.detach().cpu().float().numpy()
             steps.append(d)
-        out.append((_bank_np(torch, bank[rows]), steps))
+        out.append((_bank_np(torch, bank[used]), steps))
     return out
+
+
+def sample_streams(wl, target_streams: int, max_bytes: int = 2 << 30) -> int:
+    """Streams in an oracle sample: ``target_streams``, at most every stream, and at most
+    as many as keep the sample's touched bank rows within ``max_bytes`` of host memory."""
+    es = 2 if "bfloat16" in str(wl.bank_dtype) else 4
+    rows_per_stream = min(wl.slots_per_stream, (wl.W + wl.R) * wl.steps)
+    cap = max(1, max_bytes // (rows_per_stream * wl.head_dim * es))
+    return int(max(1, min(wl.streams, target_streams, cap)))
 
 
 def run_decode_groups(groups):
@@ -196,29 +279,33 @@ def run_decode_groups(groups):
 
 
 def cpu_baseline_decode(torch, wl, bank, seq, target_s, cfg_name):
-    """Time the oracle on a subset of streams over the whole sequence: one thread, and
-    one thread per host core over contiguous stream groups."""
+    """Time the oracle on a subset of streams over the whole sequence: one thread pinned
+    to one CPU, and one thread per host core (up to THREAD_CAP) over contiguous stream
+    groups."""
     # calibrate on 32 streams x 2 steps (enough work that fixed call costs do not
     # dominate), then size the sample for ~target_s of work
     m = min(32, wl.streams)
     (b, steps), = decode_groups(torch, wl, bank, seq[:2], m, 1)
-    t0 = time.perf_counter()
-    run_decode_groups([(b, steps)])
-    per = (time.perf_counter() - t0) / (2 * m)
-    n = int(max(1, min(wl.streams, target_s / max(per * len(seq), 1e-9))))
+    with pinned_to_one_cpu():
+        t0 = time.perf_counter()
+        run_decode_groups([(b, steps)])
+        per = (time.perf_counter() - t0) / (2 * m)
+    n = sample_streams(wl, int(target_s / max(per * len(seq), 1e-9)))
     grp = decode_groups(torch, wl, bank, seq, n, 1)
-    t0 = time.perf_counter()
-    run_decode_groups(grp)
-    dt = time.perf_counter() - t0
+    with pinned_to_one_cpu() as pin:
+        t0 = time.perf_counter()
+        run_decode_groups(grp)
+        dt = time.perf_counter() - t0
     cores = host_threads()
-    n_all = int(max(1, min(wl.streams, n * cores)))
+    n_all = sample_streams(wl, n * cores)
     grp = decode_groups(torch, wl, bank, seq, n_all, cores)
     t0 = time.perf_counter()
     run_decode_groups(grp)
     dt_all = time.perf_counter() - t0
     return {"value": n * len(seq) / dt, "unit": "stream-steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} of {wl.streams} streams x all {len(seq)} steps of {cfg_name} "
-                      f"(single-threaded C oracle, {dt:.1f} s)",
+                      f"(single-threaded C oracle pinned to CPU {pin.cpu}, {dt:.1f} s)",
+            "pinned_cpu": pin.cpu, "host": host_record(),
             "all_cores": {"value": n_all * len(seq) / dt_all, "unit": "stream-steps/s", "cores": len(grp),
                           "sample": f"{n_all} of {wl.streams} streams x all {len(seq)} steps, one thread per "
                                     f"group of streams ({dt_all:.1f} s)"}}
@@ -256,23 +343,27 @@ def run_gather_ranges(wl, sub, ranges):
         return list(ex.map(one, ranges))
 
 
-def cpu_baseline_gather(torch, wl, bank, inp, live, target_s, cfg_name):
-    """Time the oracle on the first tokens of the launch: one thread, and one thread per
-    host core over chunk-aligned token ranges."""
+def cpu_baseline_gather(torch, wl, bank, inp, target_s, cfg_name):
+    """Time the oracle on the first tokens of the launch: one thread pinned to one CPU,
+    and one thread per host core (up to THREAD_CAP) over chunk-aligned token ranges."""
     def timed(n, groups):
         sub, ranges = gather_ranges(torch, wl, bank, inp, n, groups)
         t0 = time.perf_counter()
         run_gather_ranges(wl, sub, ranges)
         return time.perf_counter() - t0, len(ranges)
 
-    per = timed(wl.chunk * 4, 1)[0] / (wl.chunk * 4)
+    with pinned_to_one_cpu():
+        per = timed(wl.chunk * 4, 1)[0] / (wl.chunk * 4)
     n = int(max(wl.chunk, min(wl.tokens, target_s / max(per, 1e-9))) // wl.chunk * wl.chunk)
-    dt, _ = timed(n, 1)
+    with pinned_to_one_cpu() as pin:
+        dt, _ = timed(n, 1)
     cores = host_threads()
     n_all = int(max(wl.chunk, min(wl.tokens, n * cores)) // wl.chunk * wl.chunk)
     dt_all, used = timed(n_all, cores)
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {wl.tokens} tokens of {cfg_name} (single-threaded C oracle, {dt:.1f} s)",
+            "sample": f"first {n} of {wl.tokens} tokens of {cfg_name} (single-threaded C oracle pinned to "
+                      f"CPU {pin.cpu}, {dt:.1f} s)",
+            "pinned_cpu": pin.cpu, "host": host_record(),
             "all_cores": {"value": n_all / dt_all, "unit": "tokens/s", "cores": used,
                           "sample": f"first {n_all} of {wl.tokens} tokens, one thread per chunk-aligned "
                                     f"range ({dt_all:.1f} s)"}}
@@ -345,7 +436,8 @@ def bench_decode(torch, args, cfg_name, wl):
                   "achieved": row_bytes_step / (ms1 / T * 1e-3) / 1e9, "frac":
                   row_bytes_step / (ms1 / T * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     return dict(value=value, unit="stream-steps/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=launch_bytes, cpu=cpu, tokens_per_s=value, single=single)
+                row_bytes=launch_bytes, cpu=cpu, tokens_per_s=value, single=single, tokens_per_launch=per_launch,
+                live_tokens=None)
 
 
 def bench_gather(torch, args, cfg_name, wl):
@@ -356,8 +448,7 @@ def bench_gather(torch, args, cfg_name, wl):
     bank = gen.gather_bank(wl, args.seed, dev)
     inp = gen.gather_inputs(wl, args.seed, dev)
     T = wl.tokens
-    t = torch.arange(T, device=dev)
-    live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
+    live = gen.live_tokens(wl, inp["chunk_valid"])
     two = args.gather in ("two-ops", "no-stash", "compact")
     with_stash = args.gather in ("two-ops", "one-op")
     compact = args.gather == "compact"
@@ -374,7 +465,7 @@ def bench_gather(torch, args, cfg_name, wl):
     torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu_baseline and args.gather == "two-ops":
-        cpu = cpu_baseline_gather(torch, wl, bank, inp, live, args.cpu_seconds, cfg_name)
+        cpu = cpu_baseline_gather(torch, wl, bank, inp, args.cpu_seconds, cfg_name)
     K = args.steps if args.steps is not None else 20
     ops = dict(idx1=inp["idx1"], w1=inp["w1"], out1=out1) if two else {}
 
@@ -400,7 +491,7 @@ def bench_gather(torch, args, cfg_name, wl):
               "launch": args.launch, "seed": args.seed}
     value = T * K / (ms * 1e-3)
     return dict(value=value, unit="tokens/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
-                row_bytes=row_bytes, cpu=cpu, tokens_per_s=value)
+                row_bytes=row_bytes, cpu=cpu, tokens_per_s=value, tokens_per_launch=T, live_tokens=live)
 
 
 def calibrate_copy(torch):
@@ -415,6 +506,28 @@ def calibrate_copy(torch):
     ms = _timed(torch, torch.cuda.current_stream(), lambda: torch.mul(src, 1.0, out=dst))
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
                       "gbps": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def dtype_fields(wl) -> dict:
+    """The arithmetic type (every sum, product and update is float32, on bfloat16 and
+    float32 banks alike) and the bank's storage type."""
+    return {"dtype": "f32", "storage_dtype": STORAGE_DTYPE[str(wl.bank_dtype)]}
+
+
+def streaming_copy_gbps(torch, mib: int = 1024, reps: int = 5) -> float:
+    """Bandwidth of a plain streaming device copy (torch's elementwise kernel copying
+    ``mib`` MiB, bytes read + written per second, best of ``reps``): what sequential traffic
+    reaches on this device, the yardstick the random-row rates are also given against."""
+    dev = torch.device("cuda", 0)
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty(n, device=dev)
+    for _ in range(2):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    best = min(_timed(torch, torch.cuda.current_stream(), lambda: torch.mul(src, 1.0, out=dst)) for _ in range(reps))
+    del src, dst
+    return 2 * n * 4 / (best * 1e-3) / 1e9
 
 
 # ------------------------------------------------------------------ profiles
@@ -448,8 +561,13 @@ def _counters(directory: str, name_part: str) -> dict:
     return {k: statistics.median(v) for k, v in vals.items()}
 
 
+SQ_SHARES = ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS",
+             "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY")
+
+
 def derived_counters(c: dict) -> dict:
-    """L2 hit rate and latencies from raw counter medians (those present)."""
+    """L2 hit rate, latencies and shares of wave time from raw counter medians (those
+    present)."""
     out = {}
     if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c and c["TCC_HIT_sum"] + c["TCC_MISS_sum"] > 0:
         out["l2_hit_rate"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
@@ -457,11 +575,19 @@ def derived_counters(c: dict) -> dict:
         out["vmem_latency_cycles"] = c["VmemLatency"]
     if c.get("TCC_EA0_RDREQ_sum", 0) > 0 and "TCC_EA0_RDREQ_LEVEL_sum" in c:
         out["ea_read_latency_cycles"] = c["TCC_EA0_RDREQ_LEVEL_sum"] / c["TCC_EA0_RDREQ_sum"]
+    if c.get("SQ_WAVE_CYCLES", 0) > 0:
+        out["wave_time_shares"] = {k: c[k] / c["SQ_WAVE_CYCLES"] for k in SQ_SHARES if k in c}
+    if "MeanOccupancyPerCU" in c:
+        out["mean_occupancy_per_cu"] = c["MeanOccupancyPerCU"]
     return out
 
 
-def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
-    """(bytes per launch, unit description) of the row traffic the method needs."""
+def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0) -> tuple:
+    """(bytes per launch, unit description, launch shape) of the row traffic the method
+    needs, for the launch the benchmark runs with these arguments. The shape holds the
+    launch's tokens per stream (decode) or its live-token count (gather); the live
+    count comes from the same draw the benchmark launches (gen draws the per-chunk
+    counts on the CPU for every device)."""
     import gen
     import torch
     wl = gen.WORKLOADS[cfg_name]
@@ -469,12 +595,13 @@ def algorithmic_bytes(cfg_name: str, entry: str) -> tuple:
     if isinstance(wl, gen.DecodeWorkload):
         per = wl.streams * (2 * wl.W + wl.R) * wl.head_dim * es
         tokens = wl.steps if entry == "steps" else 1
-        return per * tokens, f"{tokens} token(s) x {wl.streams} streams x (2W+R)={2 * wl.W + wl.R} rows x {wl.head_dim * es} B"
-    t = torch.arange(wl.tokens)
-    inp = gen.gather_inputs(wl, 0)
-    live = int(((t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]).sum())
+        return (per * tokens,
+                f"{tokens} token(s) x {wl.streams} streams x (2W+R)={2 * wl.W + wl.R} rows x {wl.head_dim * es} B",
+                {"tokens_per_launch": tokens})
+    live = gen.live_tokens(wl, gen.gather_inputs(wl.replace(width0=1, width1=0), seed)["chunk_valid"])
     rows = live * (wl.width0 + wl.width1) * wl.head_dim * es + wl.tokens * wl.width0 * wl.head_dim * es
-    return rows, f"{live} live tokens x {wl.width0 + wl.width1} rows read + {wl.tokens} x {wl.width0} stash rows, x {wl.head_dim * es} B"
+    return (rows, f"{live} live tokens x {wl.width0 + wl.width1} rows read + {wl.tokens} x {wl.width0} stash rows, "
+                  f"x {wl.head_dim * es} B", {"tokens_per_launch": wl.tokens, "live_tokens": live})
 
 
 def ingest_profile(args) -> int:
@@ -499,7 +626,7 @@ def ingest_profile(args) -> int:
     cw_kib, _ = _counter_kib(copy_write, "elementwise", min_kib=gib_kib / 8)
     f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
-    alg, alg_desc = algorithmic_bytes(args.config, args.entry)
+    alg, alg_desc, shape = algorithmic_bytes(args.config, args.entry, args.seed)
     raw = {}
     for d in args.extra_counters:
         raw.update(_counters(d, kernel))
@@ -513,7 +640,7 @@ def ingest_profile(args) -> int:
         "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fetch_b + write_b,
         "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
         "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls, "kernel": kernel,
-        "counters": raw, **derived}
+        "counters": raw, **shape, **derived}
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -547,8 +674,14 @@ def ingest_profile(args) -> int:
                         f"SQ_INSTS_VMEM) = {derived['vmem_latency_cycles']:.0f} cycles. ")
             if "ea_read_latency_cycles" in derived:
                 f.write(f"Average L2-to-memory read latency TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum = "
-                        f"{derived['ea_read_latency_cycles']:.0f} cycles.")
+                        f"{derived['ea_read_latency_cycles']:.0f} cycles. ")
+            if "mean_occupancy_per_cu" in derived:
+                f.write(f"Mean occupancy {derived['mean_occupancy_per_cu']:.1f} waves per CU (MeanOccupancyPerCU). ")
             f.write("\n")
+            if "wave_time_shares" in derived:
+                f.write("\nShares of wave time (counter / SQ_WAVE_CYCLES):\n\n| counter | share |\n|---|---|\n")
+                for k, v in derived["wave_time_shares"].items():
+                    f.write(f"| {k} | {v:.3f} |\n")
     print(json.dumps({"wrote": [traffic_path, md], "avg_kernel_us": avg_ns / 1e3,
                       "traffic_MiB": (fetch_b + write_b) / 2**20, "alg_MiB": alg / 2**20}))
     return 0
@@ -580,7 +713,8 @@ def main(argv=None):
     else:
         r = bench_gather(torch, args, args.config, wl)
     kind = launch_kind(args.config, args.entry, args.gather)
-    traffic, kernel = stored_traffic(args.config, kind)
+    traffic, kernel = stored_traffic(args.config, kind, r["tokens_per_launch"], r["live_tokens"])
+    copy_gbps = streaming_copy_gbps(torch)
     out = {
         "metric": METRIC,
         "value": r["value"],
@@ -592,18 +726,24 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        **dtype_fields(wl),
         "data": "synthetic (seeded; gen/workloads.py)",
         "config": r["config"],
         "roofline": {"bound": "hbm", "achieved": r["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": r["gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": kernel or kernel_pattern(kind), "algorithmic_bytes_per_launch": r["row_bytes"]},
+                     "kernel": kernel or kernel_pattern(kind), "algorithmic_bytes_per_launch": r["row_bytes"],
+                     "tokens_per_launch": r["tokens_per_launch"], "copy_gbps": copy_gbps,
+                     "copy_frac": r["gbps"] / copy_gbps},
         "cpu_baseline": r["cpu"],
         "tokens_per_s": r["tokens_per_s"],
         "row_gbps": r["gbps"],
     }
     if r.get("single"):
-        out["single_token"] = r["single"]
+        single = dict(r["single"])
+        traffic1, kernel1 = stored_traffic(args.config, "step", 1)
+        single.update({"kernel": kernel1 or kernel_pattern("step"), "traffic": traffic1,
+                       "copy_frac": single["achieved"] / copy_gbps})
+        out["single_token"] = single
     print(json.dumps(out), flush=True)
     return 0
 

@@ -15,5 +15,6 @@ from .workloads import (  # noqa: F401
     decode_sequence,
     gather_bank,
     gather_inputs,
+    live_tokens,
     sub_seed,
 )

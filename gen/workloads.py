@@ -248,10 +248,17 @@ def gather_inputs(wl: GatherWorkload, seed: int, device="cpu") -> dict:
         out[f"idx{o}"] = idx.to(wl.idx_dtype)
         out[f"w{o}"] = w.to(wl.w_dtype)
     chunks = T // wl.chunk if wl.chunk > 0 else 0
+    # Drawn on the CPU whatever the device, so a launch's live-token count (and with
+    # it the rows it moves) is the same number on every device.
     out["chunk_valid"] = torch.randint(wl.valid_low, wl.valid_high + 1, (chunks,),
-                                       generator=_gen(device, seed, "valid"), device=device,
-                                       dtype=torch.int32)
+                                       generator=_gen("cpu", seed, "valid"),
+                                       dtype=torch.int32).to(device)
     return out
+
+
+def live_tokens(wl: GatherWorkload, chunk_valid: torch.Tensor) -> int:
+    """Number of live (non-padding) tokens of a gather launch with these per-chunk counts."""
+    return int(chunk_valid.to("cpu", torch.int64).clamp(0, wl.chunk).sum())
 
 
 def compact_positions(idx0: torch.Tensor, chunk: int, chunk_valid: torch.Tensor) -> torch.Tensor:

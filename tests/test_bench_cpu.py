@@ -71,13 +71,78 @@ def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
     assert e["fetch_scale"] == pytest.approx(2.0) and e["write_scale"] == pytest.approx(1.0)
     assert e["bytes_per_launch"] == pytest.approx((500000.0 * 2 + 400000.0) * 1024)
     assert e["avg_kernel_ns"] == pytest.approx(300000.0)
-    alg, _ = bench.algorithmic_bytes("c1", "steps")
+    alg, _, shape = bench.algorithmic_bytes("c1", "steps")
     assert e["algorithmic_bytes_per_launch"] == alg == 64 * 1024 * 96 * 256
+    assert e["tokens_per_launch"] == shape["tokens_per_launch"] == 64
     assert (tmp_path / "profiles" / "sdm_decode_steps_wide_kernel_c1.md").exists()
-    # the stored figures apply while the kernel sources are unchanged
-    assert bench.stored_traffic("c1", "steps") == (e["bytes_per_launch"], "sdm_decode_steps_wide_kernel")
+    # the stored figures apply while the kernel sources are unchanged, scaled to the
+    # launch's token count
+    assert bench.stored_traffic("c1", "steps", 64) == (e["bytes_per_launch"], "sdm_decode_steps_wide_kernel")
+    b20, k20 = bench.stored_traffic("c1", "steps", 20)
+    assert b20 == pytest.approx(e["bytes_per_launch"] * 20 / 64) and k20 == "sdm_decode_steps_wide_kernel"
+    # a multi-token figure never stands for a single-token launch (another kernel)
+    assert bench.stored_traffic("c1", "steps", 1) == (None, None)
+    assert bench.stored_traffic("c1", "step", 1) == (None, None)
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.stored_traffic("c1", "steps") == (None, None)
+    assert bench.stored_traffic("c1", "steps", 64) == (None, None)
+
+
+def test_traffic_of_the_timed_launch_matches_its_algorithmic_bytes(tmp_path, monkeypatch):
+    """The traffic reported for a launch of K tokens is the per-token counter bytes times
+    K: its ratio to that launch's algorithmic bytes is the profiled ratio, whatever K."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    alg, _, _ = bench.algorithmic_bytes("c1", "steps")
+    _trace(t, [(WIDE, 10, 300000.0)])
+    # 1.04 x the algorithmic bytes over the 64-token launch, split 2:1 between reads and writes
+    _counter(f, [(WIDE, alg * 1.04 * 2 / 3 / 1024 / 2)])
+    _counter(w, [(WIDE, alg * 1.04 / 3 / 1024)])
+    _counter(cf, [(COPY, 524288.0)])
+    _counter(cw, [(COPY, 1048576.0)])
+    assert bench.main(["--config", "c1", "--ingest-profile", t, f, w, cf, cw]) == 0
+    per_token = alg // 64
+    for k in (2, 20, 64):
+        traffic, _ = bench.stored_traffic("c1", "steps", k)
+        assert traffic / (per_token * k) == pytest.approx(1.04)
+
+
+def test_gather_traffic_needs_the_same_live_tokens(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    g = "void sdm::(anonymous namespace)::sdm_gather_kernel<unsigned short, 16, 2, false, int, unsigned short>(sdm::GatherParams)"
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    _trace(t, [(g, 10, 250000.0)])
+    _counter(f, [(g, 700000.0)])
+    _counter(w, [(g, 600000.0)])
+    _counter(cf, [(COPY, 524288.0)])
+    _counter(cw, [(COPY, 1048576.0)])
+    assert bench.main(["--config", "c3", "--ingest-profile", t, f, w, cf, cw]) == 0
+    with open(tmp_path / "profiles" / "traffic.json") as fh:
+        e = json.load(fh)["c3/gather"]
+    _, _, shape = bench.algorithmic_bytes("c3", "steps")
+    assert e["live_tokens"] == shape["live_tokens"]
+    assert bench.stored_traffic("c3", "gather", 32768, shape["live_tokens"])[0] == pytest.approx(
+        (700000.0 * 2 + 600000.0) * 1024)
+    assert bench.stored_traffic("c3", "gather", 32768, shape["live_tokens"] - 1) == (None, None)
+
+
+def test_gather_live_count_does_not_depend_on_the_device():
+    """The profile's algorithmic bytes and the benchmark's launch count the same live
+    tokens: the per-chunk counts are drawn on the CPU for every device."""
+    import gen
+    wl = gen.WORKLOADS["c3"]
+    a = gen.gather_inputs(wl.replace(width0=1, width1=0), 0)["chunk_valid"]
+    b = gen.gather_inputs(wl.replace(width0=2, width1=3), 0)["chunk_valid"]
+    assert a.dtype == torch_int32() and a.equal(b)
+    _, _, shape = bench.algorithmic_bytes("c3", "steps")
+    assert shape["live_tokens"] == gen.live_tokens(wl, a) == int(a.long().sum())
+    with open(os.path.join(ROOT, "gen", "workloads.py")) as fh:
+        src = fh.read()
+    assert 'generator=_gen("cpu", seed, "valid")' in src
+
+
+def torch_int32():
+    import torch
+    return torch.int32
 
 
 def test_ingest_rejects_a_trace_with_both_decode_loops(tmp_path, monkeypatch):
@@ -130,7 +195,38 @@ def test_host_threads_is_bounded(monkeypatch):
     monkeypatch.setenv("OMP_NUM_THREADS", "3")
     assert bench.host_threads() == min(3, len(os.sched_getaffinity(0)))
     monkeypatch.delenv("OMP_NUM_THREADS")
-    assert 1 <= bench.host_threads() <= 16
+    assert 1 <= bench.host_threads() <= bench.THREAD_CAP == 16
+
+
+def test_host_record_names_the_cpu_and_the_cap():
+    h = bench.host_record()
+    assert h["nproc"] == os.cpu_count() and h["affinity_cpus"] == len(os.sched_getaffinity(0))
+    assert isinstance(h["model"], str) and h["model"]
+    assert h["thread_cap"] == 16 and "16" in h["thread_cap_reason"]
+
+
+def test_single_thread_leg_is_pinned_and_restored():
+    before = os.sched_getaffinity(0)
+    seen = []
+    with bench.pinned_to_one_cpu() as pin:
+        seen.append(os.sched_getaffinity(0))
+        import threading
+        th = threading.Thread(target=lambda: seen.append(os.sched_getaffinity(0)))
+        th.start()
+        th.join()
+    assert seen[0] == {pin.cpu} and seen[1] == {pin.cpu}  # threads started meanwhile inherit it
+    assert os.sched_getaffinity(0) == before
+
+
+def test_oracle_sample_is_bounded_in_host_memory():
+    import gen
+    wl = gen.WORKLOADS["c2"]
+    n = bench.sample_streams(wl, 10 ** 9)
+    # every touched row of every sampled stream fits the cap
+    assert n * (wl.W + wl.R) * wl.steps * wl.head_dim * 2 <= 2 << 30
+    assert bench.sample_streams(wl, 3) == 3 and bench.sample_streams(wl, 0) == 1
+    c1 = gen.WORKLOADS["c1"]
+    assert bench.sample_streams(c1, 10 ** 9) == c1.streams
 
 
 def test_decode_groups_give_the_whole_runs_bits():
@@ -170,3 +266,11 @@ def test_gather_ranges_give_the_whole_runs_bits():
     assert np.array_equal(np.concatenate([p[0] for p in parts]).view(np.uint32), w0.view(np.uint32))
     assert np.array_equal(np.concatenate([p[1] for p in parts]).view(np.uint16), ws.view(np.uint16))
     assert np.array_equal(np.concatenate([p[2] for p in parts]).view(np.uint32), w1.view(np.uint32))
+
+
+def test_dtype_fields():
+    """dtype is the arithmetic type (float32 on every bank); the bank's storage type is
+    reported beside it."""
+    import gen
+    assert bench.dtype_fields(gen.WORKLOADS["c2"]) == {"dtype": "f32", "storage_dtype": "bf16"}
+    assert bench.dtype_fields(gen.WORKLOADS["c4"]) == {"dtype": "f32", "storage_dtype": "f32"}
