@@ -75,31 +75,6 @@ __device__ __forceinline__ Stage carve_stage(char* base, int W, int R, int slice
     return st;
 }
 
-// Stage stream s's metadata of step t directly (loads, then LDS stores).
-template <typename E>
-__device__ __forceinline__ void stage_direct(const DecodeParams& p, int t, int64_t s, const Stage& st, int64_t col0,
-                                             int slice_cols) {
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int64_t row = int64_t(t) * p.streams + s;  // this stream's row of step t
-    for (int i = tid; i < p.W; i += nthr) {
-        const float kv = to_bank<E>(value_at(p.k_val, row * p.W + i, p.val_bytes));
-        const float d = float(exp(double(p.g[row * p.G + (p.G == 1 ? 0 : i)])));
-        st.kslot[i] = slot_at(p.k_idx, row * p.W + i, p.k_bytes);
-        st.kv[i] = kv;
-        st.d[i] = d;
-        st.coef[i] = kv * d;
-    }
-    for (int i = tid; i < p.R; i += nthr) {
-        st.qslot[i] = slot_at(p.q_idx, row * p.R + i, p.q_bytes);
-        st.qv[i] = to_bank<E>(value_at(p.q_val, row * p.R + i, p.val_bytes));
-    }
-    for (int col = tid; col < slice_cols; col += nthr) {
-        const int64_t c = col0 + col;
-        st.v[col] = c < p.hd ? to_bank<E>(value_at(p.v, row * p.hd + c, p.val_bytes)) : 0.0f;
-    }
-    if (tid == 0) st.beta[0] = p.beta[row];
-}
-
 // A step's metadata as fetched ahead by one thread, into registers: items
 // i = tid + m * threads, MK of W and R and MV of the slice's v. Every load is
 // unconditional (indices clamped to the last item), so no load sits in a
@@ -111,7 +86,10 @@ struct Meta {
     float beta;
 };
 
-template <int MK, int MV>
+// VBETA: read beta with vector loads, which issue with the others (a load from an
+// address that is the same for the whole workgroup otherwise becomes a scalar
+// load, which the compiler may schedule late).
+template <int MK, int MV, bool VBETA = false>
 __device__ __forceinline__ void meta_load(const DecodeParams& p, int t, int64_t s, int64_t col0, Meta<MK, MV>& m) {
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int64_t row = int64_t(t) * p.streams + s;
@@ -130,7 +108,7 @@ __device__ __forceinline__ void meta_load(const DecodeParams& p, int t, int64_t 
         const int64_t c = min(col0 + tid + k * nthr, p.hd - 1);
         m.vraw[k] = value_at(p.v, row * p.hd + c, p.val_bytes);
     }
-    m.beta = p.beta[row];
+    m.beta = VBETA ? value_at(p.beta, row, 4) : p.beta[row];
 }
 
 // Round fetched metadata to the bank dtype, form decays and coefficients, and
@@ -161,6 +139,19 @@ __device__ __forceinline__ void meta_store(const DecodeParams& p, const Meta<MK,
         if (col < slice_cols) st.v[col] = col0 + col < p.hd ? to_bank<E>(m.vraw[k]) : 0.0f;
     }
     if (tid == 0) st.beta[0] = m.beta;
+}
+
+// Stage stream s's metadata of step t now: every load issued at once, then
+// rounded and stored. The empty asm statement with a memory clobber keeps the
+// loads above it, so none is moved down next to its (guarded) store and waited
+// for there: the stage costs one memory round trip, not one per guarded store.
+template <typename E, int MK, int MV>
+__device__ __forceinline__ void stage_now(const DecodeParams& p, int t, int64_t s, const Stage& st, int64_t col0,
+                                          int slice_cols) {
+    Meta<MK, MV> m;
+    meta_load<MK, MV, true>(p, t, s, col0, m);
+    asm volatile("" ::: "memory");
+    meta_store<E, MK, MV>(p, m, st, col0, slice_cols);
 }
 
 // Lane geometry shared by the phases.
@@ -343,7 +334,9 @@ __device__ __forceinline__ Lane lane_geometry(const DecodeParams& p) {
 }
 
 // JN: rows a lane holds per phase (a power of two >= ceil(max(W, R) / RG)).
-template <typename E, int VB, int JN>
+// MK, MV: metadata items per thread (W, R <= MK threads; the slice's columns <=
+// MV threads).
+template <typename E, int VB, int JN, int MK, int MV>
 __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
@@ -355,7 +348,7 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
     float* dv = partial + p.rg * ln.slice_cols;
     E* bank = static_cast<E*>(p.bank);
 
-    stage_direct<E>(p, 0, s, st, ln.col0, ln.slice_cols);
+    stage_now<E, MK, MV>(p, 0, s, st, ln.col0, ln.slice_cols);
     __syncthreads();
 
     V row[JN];
@@ -398,10 +391,7 @@ __global__ __launch_bounds__(1024) void sdm_decode_steps_kernel(const DecodePara
     E* bank = static_cast<E*>(p.bank);
     const int T = p.steps;
 
-    {
-        const Stage st0 = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
-        stage_direct<E>(p, 0, s, st0, ln.col0, ln.slice_cols);
-    }
+    stage_now<E, MK, MV>(p, 0, s, carve_stage(s_raw, p.W, p.R, ln.slice_cols), ln.col0, ln.slice_cols);
     __syncthreads();
     V wrow[JN], rrow[JN];
     load_rows<E, VB, JN>(wrow, bank, carve_stage(s_raw, p.W, p.R, ln.slice_cols).kslot, p.W, p.rg, p.hd, ln);
@@ -468,7 +458,7 @@ void sdm_decode_steps_wide_kernel(const DecodeParams p) {
     // step 0's write, alone: stage, request rows, retrieval, delta_v, write-back;
     // step 1's metadata staged, step 2's fetched.
     const Stage st0 = carve_stage(s_raw, p.W, p.R, ln.slice_cols);
-    stage_direct<E>(p, 0, s, st0, ln.col0, ln.slice_cols);
+    stage_now<E, MK, MV>(p, 0, s, st0, ln.col0, ln.slice_cols);
     Meta<MK, MV> m;
     meta_load(p, min(1, T - 1), s, ln.col0, m);
     __syncthreads();
@@ -530,8 +520,10 @@ void launch_jn(const DecodeParams& p, const DecodeGeometry& geo, hipStream_t str
     const dim3 block(unsigned(geo.threads));
     const int slice_cols = geo.lpr * (VB / int(sizeof(E)));
     const bool mk1 = p.W <= geo.threads && p.R <= geo.threads && slice_cols <= geo.threads;
-    if (geo.loop == kLoopSingle)
-        hipLaunchKernelGGL((sdm_decode_kernel<E, VB, JN>), grid, block, geo.lds, stream, p);
+    if (geo.loop == kLoopSingle && mk1)
+        hipLaunchKernelGGL((sdm_decode_kernel<E, VB, JN, 1, 1>), grid, block, geo.lds, stream, p);
+    else if (geo.loop == kLoopSingle)
+        hipLaunchKernelGGL((sdm_decode_kernel<E, VB, JN, 4, 8>), grid, block, geo.lds, stream, p);
     else if (geo.loop == kLoopWide && mk1)
         hipLaunchKernelGGL((sdm_decode_steps_wide_kernel<E, VB, JN, 1, 1>), grid, block, geo.lds, stream, p);
     else if (geo.loop == kLoopWide)

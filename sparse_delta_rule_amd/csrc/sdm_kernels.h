@@ -78,6 +78,7 @@ __device__ __forceinline__ void opaque(uint4& v) {
 }
 __device__ __forceinline__ void opaque(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
 __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(float& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(uint16_t& v) {
     uint32_t w = v;
     asm volatile("" : "+v"(w));
