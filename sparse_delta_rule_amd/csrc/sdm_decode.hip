@@ -348,11 +348,29 @@ __global__ __launch_bounds__(1024) void sdm_decode_kernel(const DecodeParams p) 
     float* dv = partial + p.rg * ln.slice_cols;
     E* bank = static_cast<E*>(p.bank);
 
-    stage_now<E, MK, MV>(p, 0, s, st, ln.col0, ln.slice_cols);
-    __syncthreads();
-
     V row[JN];
-    load_rows<E, VB, JN>(row, bank, st.kslot, p.W, p.rg, p.hd, ln);
+    if constexpr (JN <= 4) {
+        // The write rows wait for this lane's own slots only, read straight from
+        // global memory; the rest of the metadata is staged under their latency.
+        Meta<MK, MV> m;
+        meta_load<MK, MV, true>(p, 0, s, ln.col0, m);
+        int64_t ks[JN];
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+            const int w = ln.grp + j * p.rg;
+            ks[j] = slot_at(p.k_idx, s * p.W + (w < p.W ? w : p.W - 1), p.k_bytes);
+        }
+#pragma unroll
+        for (int j = 0; j < JN; ++j) row[j] = *reinterpret_cast<const V*>(bank + ks[j] * p.hd + ln.vcol);
+        asm volatile("" ::: "memory");
+        meta_store<E, MK, MV>(p, m, st, ln.col0, ln.slice_cols);
+        __syncthreads();
+    } else {
+        // (eight rows per lane: the slots' registers would cost occupancy)
+        stage_now<E, MK, MV>(p, 0, s, st, ln.col0, ln.slice_cols);
+        __syncthreads();
+        load_rows<E, VB, JN>(row, bank, st.kslot, p.W, p.rg, p.hd, ln);
+    }
     row_partials<E, VB, JN>(row, st.coef, p.W, p.rg, ln, partial);
     __syncthreads();
     form_delta(p, st, partial, dv, ln);
