@@ -16,7 +16,10 @@ four passes of it, timed back to back (any K is accepted: whole passes, then
 the sequence's first K mod T tokens in one more launch); ``--entry step``
 launches sdm_decode_step once per token instead (K defaults to one pass). The timed launches run as one HIP-graph replay (``--launch
 eager`` launches from Python instead) bracketed by HIP events on the stream
-the kernels run on.
+the kernels run on. Before each timed leg the device is first kept busy with
+plain copies for --settle-ms (100 ms by default), so that its clocks are out of
+any idle state (the CPU baseline before it leaves the device idle for seconds);
+then come the W warm-up steps.
 
 Prints one JSON line: stream-steps/s (tokens/s for the gather), the achieved
 bank-row bandwidth against the MI355X's 8 TB/s HBM peak, and the CPU oracle
@@ -112,6 +115,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's sequence)")
     p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="before each timed leg, keep the device busy with plain copies for this long (0: none)")
     p.add_argument("--config", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--launch", default="graph", choices=["graph", "eager"])
@@ -123,6 +128,23 @@ def parse_args(argv=None):
                    help="gather launch shape on the c3 tokens: both operands with the stash (the workload), "
                         "operand 0 only (the backward's gather), either without the stash, or both operands "
                         "with a compact stash (sdm_gather_compact, positions from each chunk's sorted slots)")
+    p.add_argument("--streams", default=None, metavar="N[,N...]",
+                   help="decode: run the workload with N streams instead (each stream keeps its slot range, so "
+                        "the bank holds N x slots-per-stream rows); a list runs each in turn, one line each")
+    p.add_argument("--ingest-stream-sweep", metavar="TRACE",
+                   help="summarise a rocprofv3 kernel trace of a --streams sweep into profiles/ (no GPU): the "
+                        "kernel's duration per stream count, and its fit as a fixed cost plus a cost per stream")
+    p.add_argument("--ceiling", default=None, metavar="MODE[,MODE...]",
+                   help="measure reference access patterns instead of the method (libsdm_ceiling): read, stash, "
+                        "rmw, mix (two row reads and one row write per unit, the decode's mix), copy or copy-nt "
+                        "(non-temporal); one line per pattern and bank size")
+    p.add_argument("--bank-gib", default="16", metavar="G[,G...]", help="with --ceiling: bank sizes in GiB")
+    p.add_argument("--row-bytes", type=int, default=256, help="with --ceiling: bytes per row")
+    p.add_argument("--ceiling-layout", default="uniform", choices=["uniform", "streams"],
+                   help="with --ceiling: rows uniform over the bank, or (rmw, mix) laid out as the decode's c2 "
+                        "streams: each run of 64 units draws its rows from its own range of 16384 slots")
+    p.add_argument("--ingest-ceiling", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="summarise rocprofv3 output of one --ceiling run (one bank size) into profiles/ (no GPU)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -147,9 +169,29 @@ def _timed(torch, stream, fn):
     return start.elapsed_time(end)  # ms
 
 
+def settle_device(torch, ms: float) -> None:
+    """Keep the device busy with plain 256 MiB copies for about ``ms`` milliseconds, so
+    that its clocks have left any idle state before a measurement (after the CPU
+    baseline, for instance, the device has idled for seconds). Outside every timed
+    region, and on buffers of its own."""
+    if ms <= 0:
+        return
+    n = (256 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+    del a, b
+
+
 def _run_steps(torch, args, launch_one, K):
-    """Warm up, then time K launches (as one graph replay, or eagerly). Returns ms."""
+    """Settle the device, warm up, then time K launches (as one graph replay, or
+    eagerly). Returns ms."""
     stream = torch.cuda.current_stream()
+    settle_device(torch, args.settle_ms)
     for i in range(args.warmup):
         launch_one(i)
     torch.cuda.synchronize()
@@ -414,7 +456,10 @@ def bench_decode(torch, args, cfg_name, wl):
     ms_step = ms / K
     launch_bytes = row_bytes_step * per_launch
     gbps = row_bytes_step * K / (ms * 1e-3) / 1e9  # = bytes per launch / mean launch time
-    config = {"workload": f"{cfg_name}: {wl.name}", "streams": wl.streams, "slots": wl.num_slots,
+    name = f"{cfg_name}: {wl.name}"
+    if wl.streams != gen.WORKLOADS[cfg_name].streams:
+        name += f" [{wl.streams} streams]"
+    config = {"workload": name, "streams": wl.streams, "slots": wl.num_slots,
               "head_dim": wl.head_dim, "W": wl.W, "R": wl.R, "G": wl.G,
               "bank_dtype": str(wl.bank_dtype).replace("torch.", ""), "index_dtype":
               str(wl.idx_dtype).replace("torch.", ""), "sequence_steps": T,
@@ -528,6 +573,125 @@ def streaming_copy_gbps(torch, mib: int = 1024, reps: int = 5) -> float:
     best = min(_timed(torch, torch.cuda.current_stream(), lambda: torch.mul(src, 1.0, out=dst)) for _ in range(reps))
     del src, dst
     return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ ceiling
+CEILING_LAUNCHES = 8
+CEILING_KERNEL = {"read": "ceiling_rows_kernel<0", "stash": "ceiling_rows_kernel<1", "rmw": "ceiling_rows_kernel<2",
+                  "mix": "ceiling_rows_kernel<3", "copy": "ceiling_copy_kernel<8, false",
+                  "copy-nt": "ceiling_copy_kernel<8, true"}
+
+
+CEILING_STREAM_SLOTS, CEILING_STREAM_UNITS = 16384, 64
+
+
+def ceiling_plan(mode: str, bank_gib: float, row_bytes: int, layout: str = "uniform") -> tuple:
+    """(units per launch, rows per unit list entry, bytes moved per launch) of one reference
+    pattern: 2M random rows read (read, stash), 1M distinct rows rewritten (rmw), 1M
+    units of one rewritten and one read row (mix), or a 1 GiB copy. Rows never repeat
+    across the timed launches of rmw and mix. With the streams layout (rmw, mix) the
+    bank is split into streams of CEILING_STREAM_SLOTS slots, and every stream has
+    CEILING_STREAM_UNITS units per launch with distinct rows from its own slots (for
+    mix on a 16 GiB bank of 256-byte rows: the decode's c2 step, 192 MiB)."""
+    num_rows = int(bank_gib * (1 << 30)) // row_bytes
+    if mode.startswith("copy"):
+        return 0, 0, 2 << 30
+    per_unit = 2 if mode == "mix" else 1
+    if layout == "streams" and mode in ("rmw", "mix"):
+        n = num_rows // CEILING_STREAM_SLOTS * CEILING_STREAM_UNITS
+    else:
+        n = {"read": 2 << 20, "stash": 2 << 20, "rmw": 1 << 20, "mix": 1 << 20}[mode]
+        if mode in ("rmw", "mix"):
+            n = min(n, num_rows // (per_unit * (CEILING_LAUNCHES + 2)))
+    moved = {"read": 1, "stash": 2, "rmw": 2, "mix": 3}[mode] * n * row_bytes
+    return n, per_unit, moved
+
+
+def ceiling_stream_rows(torch, num_rows: int, per_unit: int, gen, dev):
+    """One launch's row list in the streams layout: for each stream, CEILING_STREAM_UNITS
+    units whose per_unit rows are distinct slots of the stream's own range (written rows
+    first in each pair, as in the decode, where a stream's write and read slots are
+    drawn from its range)."""
+    streams = num_rows // CEILING_STREAM_SLOTS
+    k = CEILING_STREAM_UNITS * per_unit
+    out = torch.empty((streams, k), dtype=torch.int64, device=dev)
+    step = max(1, (1 << 24) // CEILING_STREAM_SLOTS)
+    for s0 in range(0, streams, step):
+        m = min(step, streams - s0)
+        keys = torch.rand((m, CEILING_STREAM_SLOTS), generator=gen, device=dev)
+        out[s0:s0 + m] = keys.topk(k, dim=1).indices
+    out += torch.arange(streams, device=dev)[:, None] * CEILING_STREAM_SLOTS
+    if per_unit == 2:  # pair unit u's written row with its read row
+        out = torch.stack([out[:, :CEILING_STREAM_UNITS], out[:, CEILING_STREAM_UNITS:]], dim=2)
+    return out.reshape(-1).contiguous()
+
+
+def bench_ceiling(torch, args) -> int:
+    """Time each reference pattern on banks of the given sizes: after about 50 ms of the
+    same launches untimed, CEILING_LAUNCHES launches between HIP events, each on its own
+    random rows (uniform with repetition for read and
+    stash; for rmw and mix, distinct rows never reused across launches, or the streams
+    layout)."""
+    from sparse_delta_rule_amd import ceiling
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    copy_gbps = None
+    for gib in [float(x) for x in args.bank_gib.split(",")]:
+        num_rows = int(gib * (1 << 30)) // args.row_bytes
+        bank = torch.empty((num_rows, args.row_bytes // 4), dtype=torch.int32, device=dev)
+        bank.random_()
+        sink = torch.empty(ceiling.sink_words(), dtype=torch.int32, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed)
+        for mode in args.ceiling.split(","):
+            layout = args.ceiling_layout if mode in ("rmw", "mix") else "uniform"
+            n, per_unit, moved = ceiling_plan(mode, gib, args.row_bytes, layout)
+            L = CEILING_LAUNCHES
+            if mode.startswith("copy"):
+                half = bank.view(-1)[: (1 << 30) // 4 * 2]
+                src, dst = half[: (1 << 30) // 4], half[(1 << 30) // 4:]
+                nt = mode == "copy-nt"
+                launches = [lambda: ceiling.copy(dst, src, nontemporal=nt)] * (L + 1)
+            else:
+                if mode in ("read", "stash"):
+                    lists = torch.randint(0, num_rows, ((L + 1), n), generator=gen, device=dev)
+                elif layout == "streams":
+                    lists = torch.stack([ceiling_stream_rows(torch, num_rows, per_unit, gen, dev)
+                                         for _ in range(L + 1)])
+                else:
+                    perm = torch.randperm(num_rows, generator=gen, device=dev)
+                    lists = perm[: (L + 1) * n * per_unit].view(L + 1, n * per_unit)
+                    del perm
+                stash = torch.empty((n, args.row_bytes // 4), dtype=torch.int32, device=dev) \
+                    if mode == "stash" else None
+                launches = [(lambda i=i: ceiling.rows(mode, bank, lists[i], stash=stash, sink=sink))
+                            for i in range(L + 1)]
+            # untimed: the pattern's first launch, then ~50 ms more of it (the device's clocks
+            # settle after tens of milliseconds of load)
+            launches[0]()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.05:
+                for f in launches[1:]:
+                    f()
+                torch.cuda.synchronize()
+            ms = _timed(torch, stream, lambda: [f() for f in launches[1:]]) / L
+            gbps = moved / (ms * 1e-3) / 1e9
+            if mode.startswith("copy"):
+                copy_gbps = max(copy_gbps or 0.0, gbps)
+            line = {"metric": f"reference access pattern on one MI355X: {mode}", "mode": mode, "bank_gib": gib,
+                    "row_bytes": args.row_bytes, "layout": layout, "units_per_launch": n, "bytes_per_launch": moved,
+                    "launches": L, "us_per_launch": ms * 1e3, "achieved": gbps, "unit": "GB/s",
+                    "peak": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS,
+                    "kernel": CEILING_KERNEL[mode].split("<")[0]}
+            if copy_gbps and not mode.startswith("copy"):
+                line["copy_frac"] = gbps / copy_gbps
+            print(json.dumps(line), flush=True)
+            del launches
+            torch.cuda.empty_cache()
+        del bank, sink
+        torch.cuda.empty_cache()
+    return 0
 
 
 # ------------------------------------------------------------------ profiles
@@ -687,11 +851,150 @@ def ingest_profile(args) -> int:
     return 0
 
 
+def _trace_dispatches(directory: str, name_part: str):
+    """(workgroups, duration ns) of every dispatch in a rocprofv3 kernel trace whose
+    kernel name contains name_part."""
+    out = []
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        if name_part in r["Kernel_Name"]:
+            wgs = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) * int(r["Grid_Size_Y"])
+            out.append((wgs, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def fit_line(xs, ys):
+    """Least-squares (intercept, slope) of ys against xs."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    return my - slope * mx, slope
+
+
+def ingest_stream_sweep(args) -> int:
+    """Kernel durations of a --streams sweep, per stream count, and their fit as a fixed
+    cost per launch plus a cost per stream (whose bytes give the marginal bandwidth)."""
+    import statistics
+    import gen
+    import torch
+    wl = gen.WORKLOADS[args.config]
+    if not isinstance(wl, gen.DecodeWorkload):
+        raise SystemExit("bench.py: a stream sweep is a decode measurement")
+    kind = launch_kind(args.config, args.entry)
+    pattern = kernel_pattern(kind)
+    disp = _trace_dispatches(args.ingest_stream_sweep, pattern)
+    if not disp:
+        raise SystemExit(f"bench.py: no {pattern} dispatch in {args.ingest_stream_sweep}")
+    tokens = wl.steps if kind == "steps" else 1
+    es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    per_stream = (2 * wl.W + wl.R) * wl.head_dim * es * tokens
+    by_wgs = {}
+    for wgs, ns in disp:
+        by_wgs.setdefault(wgs, []).append(ns)
+    # launch sizes in workgroups, matched in order to the sweep's stream counts
+    counts = sorted(int(x) for x in args.streams.split(",")) if args.streams else None
+    groups = sorted(by_wgs)
+    if counts is None or len(counts) != len(groups):
+        raise SystemExit(f"bench.py: pass the sweep's --streams list ({len(groups)} launch sizes in the trace)")
+    rows = [(n, wg, statistics.median(by_wgs[wg]), len(by_wgs[wg])) for n, wg in zip(counts, groups)]
+    icpt, slope = fit_line([r[0] for r in rows], [r[2] for r in rows])
+    marginal = per_stream / slope  # bytes per ns = GB/s
+    md = os.path.join(PROFILES, f"{re.sub(r'[^a-z_]', '', pattern)}_{args.config}_stream_sweep.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(md, "w") as f:
+        f.write(f"# {pattern} on workload {args.config} over stream counts (MI355X, rocprofv3 kernel trace)\n\n")
+        f.write(f"Kernel sources hash {kernel_source_hash()} (bench.py `kernel_source_hash`). Each stream keeps "
+                f"its {wl.slots_per_stream} slots, so the bank grows with the stream count; {tokens} token(s) per "
+                f"launch, {per_stream} algorithmic row bytes per stream per launch.\n\n")
+        f.write("## Command\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")
+        f.write("## Median kernel duration per launch size\n\n| streams | workgroups | launches | median duration "
+                "| row bytes | rate | fraction of 8 TB/s |\n|---|---|---|---|---|---|---|\n")
+        for n, wg, med, k in rows:
+            b = n * per_stream
+            f.write(f"| {n} | {wg} | {k} | {med / 1e3:.2f} us | {b / 2**20:.1f} MiB | {b / med:.0f} GB/s | "
+                    f"{b / med / HBM_PEAK_GBPS:.3f} |\n")
+        f.write(f"\nLeast-squares fit: duration = {icpt / 1e3:.2f} us + streams x {slope:.2f} ns. The fixed part is "
+                f"the cost of a launch whatever its size; the part per stream moves {per_stream} row bytes, a "
+                f"marginal rate of {marginal:.0f} GB/s ({marginal / HBM_PEAK_GBPS:.3f} of the 8 TB/s peak).\n")
+    print(json.dumps({"wrote": md, "fixed_us": icpt / 1e3, "ns_per_stream": slope, "marginal_gbps": marginal,
+                      "rows": rows}))
+    return 0
+
+
+def ingest_ceiling(args) -> int:
+    """Kernel durations and HBM bytes of one --ceiling run (one bank size): per pattern,
+    the rate its algorithmic bytes reach in the kernel trace and the counters' bytes."""
+    trace, fetch, write, copy_fetch, copy_write = args.ingest_ceiling
+    gib = float(args.bank_gib)
+    stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if "ceiling_" in r["Name"]]
+    gib_kib = float(1 << 20)
+    cf_kib, _ = _counter_kib(copy_fetch, "elementwise", min_kib=gib_kib / 8)
+    cw_kib, _ = _counter_kib(copy_write, "elementwise", min_kib=gib_kib / 8)
+    f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
+    out = {}
+    for mode, frag in CEILING_KERNEL.items():
+        rows = [r for r in stats if frag in r["Name"]]
+        if not rows:
+            continue
+        calls = sum(int(r["Calls"]) for r in rows)
+        avg_ns = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in rows) / calls
+        n, _, moved = ceiling_plan(mode, gib, args.row_bytes,
+                                   args.ceiling_layout if mode in ("rmw", "mix") else "uniform")
+        f_kib, _ = _counter_kib(fetch, frag)
+        w_kib, _ = _counter_kib(write, frag)
+        out[mode] = {"avg_kernel_ns": avg_ns, "calls": calls, "bytes_per_launch": moved, "units_per_launch": n,
+                     "frac": moved / avg_ns / HBM_PEAK_GBPS, "fetch_bytes": f_kib * 1024 * f_scale,
+                     "write_bytes": w_kib * 1024 * w_scale}
+    if not out:
+        raise SystemExit(f"bench.py: no ceiling kernel in {trace}")
+    path = os.path.join(PROFILES, "ceiling.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[f"{gib:g}GiB/{args.row_bytes}B/{args.ceiling_layout}"] = out
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    md = os.path.join(PROFILES, f"sdm_ceiling_bank_{gib:g}gib_rows_{args.row_bytes}b_{args.ceiling_layout}.md")
+    with open(md, "w") as f:
+        f.write(f"# Reference access patterns over a {gib:g} GiB bank of {args.row_bytes}-byte rows "
+                "(MI355X, rocprofv3)\n\n")
+        f.write("Kernels of `sparse_delta_rule_amd/ceiling/sdm_ceiling.hip` (libsdm_ceiling): rows at uniformly "
+                "random slots, 16-byte vectors on consecutive lanes, a batch of rows in flight per lane group. "
+                "read: rows read (2M per launch, with repetition); stash: rows read and written to a sequential "
+                "stash; rmw: distinct rows read and written back in place; mix: per unit one row read and "
+                "written back and one other row read (the decode's mix of two row reads per row write); copy: a "
+                "sequential 1 GiB copy (copy-nt: non-temporal loads and stores). Layout of the rmw and mix rows: "
+                f"{args.ceiling_layout} (uniform: over the whole bank, never reused across launches; streams: "
+                f"runs of {CEILING_STREAM_UNITS} units draw distinct rows from their own {CEILING_STREAM_SLOTS} "
+                "slots, as the decode's streams do).\n\n")
+        f.write("## Commands\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")
+        f.write("| pattern | launches | average duration | bytes moved per launch | rate | fraction of 8 TB/s | "
+                "FETCH_SIZE bytes | WRITE_SIZE bytes | counted / moved |\n|---|---|---|---|---|---|---|---|---|\n")
+        for mode, e in out.items():
+            cnt = e["fetch_bytes"] + e["write_bytes"]
+            f.write(f"| {mode} | {e['calls']} | {e['avg_kernel_ns'] / 1e3:.1f} us | {e['bytes_per_launch'] / 2**20:.0f} "
+                    f"MiB | {e['bytes_per_launch'] / e['avg_kernel_ns']:.0f} GB/s | {e['frac']:.3f} | "
+                    f"{e['fetch_bytes'] / 2**20:.0f} MiB | {e['write_bytes'] / 2**20:.0f} MiB | "
+                    f"{cnt / e['bytes_per_launch']:.3f} |\n")
+        f.write(f"\nCounter scales from a plain 1 GiB copy measured the same way: FETCH_SIZE x {f_scale:.4f}, "
+                f"WRITE_SIZE x {w_scale:.4f}.\n")
+    print(json.dumps({"wrote": [path, md], **{m: round(e["frac"], 4) for m, e in out.items()}}))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.ingest_profile:
         sys.path.insert(0, ROOT)
         return ingest_profile(args)
+    if args.ingest_stream_sweep:
+        sys.path.insert(0, ROOT)
+        return ingest_stream_sweep(args)
+    if args.ingest_ceiling:
+        sys.path.insert(0, ROOT)
+        return ingest_ceiling(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: the benchmark measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
@@ -706,8 +1009,28 @@ def main(argv=None):
     if args.calibrate_copy:
         calibrate_copy(torch)
         return 0
+    if args.ceiling:
+        return bench_ceiling(torch, args)
     import gen
     wl = gen.WORKLOADS[args.config]
+    if args.streams is not None:
+        if not isinstance(wl, gen.DecodeWorkload):
+            raise SystemExit("bench.py: --streams applies to the decode workloads")
+        counts = [int(x) for x in args.streams.split(",")]
+        if len(counts) > 1:
+            for n in counts:
+                sub = argparse.Namespace(**{**vars(args), "streams": str(n)})
+                rc = main_one(torch, gen, sub, wl.replace(streams=n))
+                torch.cuda.empty_cache()
+                if rc:
+                    return rc
+            return 0
+        wl = wl.replace(streams=counts[0])
+    return main_one(torch, gen, args, wl)
+
+
+def main_one(torch, gen, args, wl) -> int:
+    """One benchmark line for one workload."""
     if isinstance(wl, gen.DecodeWorkload):
         r = bench_decode(torch, args, args.config, wl)
     else:

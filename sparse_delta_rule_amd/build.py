@@ -3,7 +3,9 @@
     python -m sparse_delta_rule_amd.build
 
 The library is built in-tree, next to this file, from csrc/*.hip; then the
-plain C example caller in examples/ is compiled against it.
+plain C example caller in examples/ is compiled against it, and the reference
+access patterns that the benchmark measures the rows' ceiling with
+(ceiling/*.hip) are built into libsdm_ceiling.so.
 """
 
 from __future__ import annotations
@@ -16,6 +18,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsdm.so")
+CEILING_LIB = os.path.join(HERE, "libsdm_ceiling.so")
 ARCH = os.environ.get("SDM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -60,18 +63,28 @@ def build_example(verbose: bool = False) -> str:
     return EXAMPLE
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(out: str, srcs: list, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode}) building {LIB}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {out}")
+    os.replace(tmp, out)
+    return out
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    return _hipcc(CEILING_LIB, sorted(glob.glob(os.path.join(HERE, "ceiling", "*.hip"))), verbose)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(LIB, sources(), verbose)
     build_example(verbose)
+    build_ceiling(verbose)
     return LIB
 
 

@@ -274,3 +274,29 @@ def test_dtype_fields():
     import gen
     assert bench.dtype_fields(gen.WORKLOADS["c2"]) == {"dtype": "f32", "storage_dtype": "bf16"}
     assert bench.dtype_fields(gen.WORKLOADS["c4"]) == {"dtype": "f32", "storage_dtype": "f32"}
+
+
+def test_stream_sweep_fit(tmp_path, monkeypatch):
+    """A kernel trace of a stream sweep is grouped by launch size and fitted as a fixed
+    cost per launch plus a cost per stream."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    name = "void sdm::(anonymous namespace)::sdm_decode_kernel<unsigned short, 16, 4, 1, 1>(sdm::DecodeParams)"
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X", "Grid_Size_Y"]
+    rows = []
+    t = 0
+    for n in (512, 1024, 2048):
+        for _ in range(3):
+            dur = 5000 + 10 * n  # 5 us fixed + 10 ns per stream
+            rows.append([name, t, t + dur, 256, n * 256, 1])
+            rows.append(["other_kernel", t, t + 7, 64, 64, 1])
+            t += dur + 100
+    d = tmp_path / "trace"
+    _write_csv(str(d / "run_kernel_trace.csv"), hdr, rows)
+    assert bench.main(["--config", "c2", "--entry", "step", "--streams", "2048,512,1024",
+                       "--ingest-stream-sweep", str(d)]) == 0
+    md = (tmp_path / "profiles" / "sdm_decode_kernel_c2_stream_sweep.md").read_text()
+    assert "5.00 us + streams x 10.00 ns" in md
+    # c2 moves (2*64 + 64) rows of 256 bytes per stream per token: 49152 B per 10 ns
+    assert "marginal rate of 4915 GB/s" in md
+    with pytest.raises(SystemExit, match="--streams list"):
+        bench.main(["--config", "c2", "--entry", "step", "--streams", "512,1024", "--ingest-stream-sweep", str(d)])
