@@ -26,7 +26,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 2 /* 2: adds sdm_gather_compact and the gather plan */
+#define SDM_ABI_VERSION 3 /* 2: adds sdm_gather_compact and the gather plan; 3: sdm_round_bf16 */
 #define SDM_MAX_WIDTH 256 /* largest W, R and gather width */
 
 /* Element types (sdm_dtype). */
@@ -277,6 +277,20 @@ const char* sdm_last_error(void);
 
 /* SDM_ABI_VERSION of the library. */
 int sdm_abi_version(void);
+
+/*
+ * sdm_round_bf16: out[i] = the bfloat16 bits of in[i], rounded as every kernel of
+ * this library rounds a float32 it stores in a bfloat16 bank or returns as a
+ * bfloat16 reading: to nearest, ties to even, denormals kept, a NaN kept a NaN
+ * with its sign and its high payload bits and the quiet bit set (page
+ * "sparse_delta_memory/decode.py": the decode kernel's casts to the bank dtype).
+ * Exposed so that the conversion can be checked on its own against a reference.
+ * in: [n] float32 (8-byte aligned), out: [n] bfloat16 bits (4-byte aligned),
+ * device pointers owned by the caller, not overlapping. Asynchronous on
+ * hip_stream. Errors: SDM_E_SHAPE (n < 0), SDM_E_NULL, SDM_E_ALIGN,
+ * SDM_E_OVERLAP, SDM_E_HIP.
+ */
+int sdm_round_bf16(const float* in, uint16_t* out, int64_t n, void* hip_stream);
 
 #ifdef __cplusplus
 }

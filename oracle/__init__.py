@@ -75,6 +75,8 @@ def _load():
     lib.oracle_float_to_bf16.restype = ctypes.c_uint16
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_float_to_bf16_array.argtypes = [P, P, i64]
+    lib.oracle_float_to_bf16_array.restype = None
     lib.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_float.restype = ctypes.c_float
     for f in (lib.sdm_oracle_decode_step, lib.sdm_oracle_decode_step_f64, lib.sdm_oracle_gather,
@@ -111,6 +113,14 @@ def _i64(x):
 
 def float_to_bf16(x: float) -> int:
     return int(_load().oracle_float_to_bf16(float(x)))
+
+
+def float_to_bf16_array(x: np.ndarray) -> np.ndarray:
+    """oracle_float_to_bf16 of every element of a float32 array (uint16 bits)."""
+    x = _f32(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_float_to_bf16_array(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 def double_to_bf16(x: float) -> int:

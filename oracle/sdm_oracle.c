@@ -86,6 +86,11 @@ uint16_t oracle_float_to_bf16(float f) {
     return (uint16_t)keep;
 }
 
+/* oracle_float_to_bf16 over an array (for checking a conversion over many inputs). */
+void oracle_float_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_float_to_bf16(in[i]);
+}
+
 /* Round a double straight to bfloat16 (one rounding, to nearest, ties to even). */
 uint16_t oracle_double_to_bf16(double x) {
     if (isnan(x)) return 0x7fc0u;

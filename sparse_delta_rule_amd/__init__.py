@@ -28,4 +28,5 @@ from ._binding import (  # noqa: F401
     sdm_gather,
     sdm_gather_compact,
     sdm_gather_plan,
+    sdm_round_bf16,
 )

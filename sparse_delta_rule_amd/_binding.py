@@ -71,12 +71,30 @@ def library() -> ctypes.CDLL:
     lib.sdm_last_error.restype = ctypes.c_char_p
     lib.sdm_abi_version.argtypes = []
     lib.sdm_abi_version.restype = ctypes.c_int
+    lib.sdm_round_bf16.argtypes = [P, P, i64, P]
+    lib.sdm_round_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 def abi_version() -> int:
     return int(library().sdm_abi_version())
+
+
+def sdm_round_bf16(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bfloat16 of every float32 of x, rounded as the library's kernels round what they
+    store (sdm_round_bf16)."""
+    if x.dtype != torch.float32 or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 device tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or out.device != x.device or not out.is_contiguous() or out.numel() != x.numel():
+        raise ValueError("out must be a contiguous bfloat16 tensor like x on its device")
+    rc = library().sdm_round_bf16(x.data_ptr(), out.data_ptr(), x.numel(),
+                                  torch.cuda.current_stream(x.device).cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
 
 
 def _raise(status: int):

@@ -267,6 +267,19 @@ const char* sdm_last_error(void) { return g_last_error.c_str(); }
 
 int sdm_abi_version(void) { return SDM_ABI_VERSION; }
 
+int sdm_round_bf16(const float* in, uint16_t* out, int64_t n, void* hip_stream) {
+    if (n < 0) return fail(SDM_E_SHAPE, "sdm_round_bf16: n = %lld < 0", (long long)n);
+    if (n == 0) return ok();
+    if (in == nullptr || out == nullptr) return fail(SDM_E_NULL, "sdm_round_bf16: in and out are required");
+    if (!aligned(in, 8) || !aligned(out, 4))
+        return fail(SDM_E_ALIGN, "sdm_round_bf16: in must be 8-byte and out 4-byte aligned");
+    if (!mul_fits(n, 1, 4)) return fail(SDM_E_SHAPE, "sdm_round_bf16: n overflows 64-bit byte counts");
+    if (overlap(in, n * 4, out, n * 2)) return fail(SDM_E_OVERLAP, "sdm_round_bf16: in and out overlap");
+    hipError_t e = sdm::launch_round_bf16(in, out, n, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SDM_E_HIP, "sdm_round_bf16: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"
 
 namespace {

@@ -224,4 +224,7 @@ GatherGeometry gather_geometry(int es, int64_t hd, uintptr_t bank_addr, uintptr_
 hipError_t launch_gather(const GatherParams& p, const GatherGeometry& geo, bool bf16, bool two,
                          hipStream_t stream);
 
+// ------------------------------------------------------------------ conversion
+hipError_t launch_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+
 }  // namespace sdm

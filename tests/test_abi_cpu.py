@@ -33,7 +33,25 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["sdm_abi_version", "sdm_decode_step", "sdm_decode_steps",
                                      "sdm_gather", "sdm_gather_compact", "sdm_gather_plan_init",
-                                     "sdm_gather_plan_launch", "sdm_last_error"]
+                                     "sdm_gather_plan_launch", "sdm_last_error", "sdm_round_bf16"]
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((A, A + MB, -1), E_SHAPE, "n = -1 < 0"),
+    ((None, A + MB, 4), E_NULL, "in and out are required"),
+    ((A, None, 4), E_NULL, "in and out are required"),
+    ((A + 4, A + MB, 4), E_ALIGN, "8-byte"),
+    ((A, A + MB + 2, 4), E_ALIGN, "4-byte"),
+    ((A, A + 8, 4), E_OVERLAP, "overlap"),
+])
+def test_round_bf16_rejects_bad_arguments(args, code, msg):
+    lib = sdm.library()
+    assert lib.sdm_round_bf16(*args, None) == code
+    assert msg in lib.sdm_last_error().decode()
+
+
+def test_round_bf16_of_nothing_is_ok():
+    assert sdm.library().sdm_round_bf16(A, A + MB, 0, None) == OK
 
 
 def test_library_exports_every_declared_symbol():

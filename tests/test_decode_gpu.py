@@ -31,8 +31,15 @@ def _say(*a):
 
 
 def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, device_inputs=False,
-                 steps=None):
-    """Run ``wl`` on the GPU over all streams and check the sampled streams both ways."""
+                 steps=None, drift_streams=()):
+    """Run ``wl`` on the GPU over all streams and check the sampled streams both ways.
+
+    drift_streams: streams the GPU runs free that are compared, every step, with the
+    oracle run free in plain ascending order from the same starting bank; the
+    largest error as a multiple of the per-step bound (magnitudes from the float64
+    brute force on the oracle's state) is returned as worst["drift_read"] and
+    worst["drift_row"], and no bound is asserted here (two correct orders drift
+    apart as errors compound)."""
     steps = wl.steps if steps is None else steps
     P = wl.slots_per_stream
     bf16 = wl.bank_dtype == torch.bfloat16
@@ -40,13 +47,16 @@ def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, 
     bank = gen.decode_bank(wl, seed, gen_dev).to(DEV)
     free_streams = np.asarray(free_streams, dtype=np.int64)
     sync_streams = np.asarray(sync_streams, dtype=np.int64)
-    assert not set(free_streams) & set(sync_streams)
+    drift_streams = np.asarray(drift_streams, dtype=np.int64)
+    assert not set(free_streams) & set(sync_streams) and not set(drift_streams) & set(sync_streams)
+    drift_rows = torch.from_numpy(stream_rows(drift_streams, P)).to(DEV)
+    bank_drift = to_np_bank(bank[drift_rows])    # oracle, ascending order, free-running
     free_rows = torch.from_numpy(stream_rows(free_streams, P)).to(DEV)
     sync_rows = torch.from_numpy(stream_rows(sync_streams, P)).to(DEV)
     bank_free = to_np_bank(bank[free_rows])      # oracle, kernel order, free-running
     bank_sync = to_np_bank(bank[sync_rows])      # oracle, ascending order, resynced into the GPU
     rg = documented_decode_groups(wl.W, wl.R)
-    worst = {"read": 0.0, "row": 0.0}
+    worst = {"read": 0.0, "row": 0.0, "drift_read": 0.0, "drift_row": 0.0}
     for t in range(steps):
         inp = gen.decode_step_inputs(wl, seed, t, gen_dev)
         inp = {k: v.to(DEV) for k, v in inp.items()}
@@ -78,6 +88,17 @@ def check_decode(wl: gen.DecodeWorkload, seed: int, free_streams, sync_streams, 
             assert ok, f"step {t}: written rows outside tolerance (worst {ratio:.3g} of the bound)"
             untouched = np.setdiff1d(np.arange(bank_sync.shape[0]), sub["k_idx"].ravel())
             assert bits_equal(got_bank[untouched], before[untouched]), f"step {t}: untouched rows changed"
+        # free-running streams against the free-running ascending-order oracle
+        if len(drift_streams):
+            sub = sub_inputs(npin, drift_streams, P)
+            _, _, row_mag, _, read_mag = oracle.decode_step_f64(bank_drift.copy(), **sub)
+            ref = oracle.decode_step(bank_drift, **sub, groups=1)
+            got = to_np_bank(readings[torch.from_numpy(drift_streams).to(DEV)])
+            _, ratio = decode_tolerance_ok(got, ref, read_mag, bf16)
+            worst["drift_read"] = max(worst["drift_read"], ratio)
+            got_bank = to_np_bank(bank[drift_rows])
+            _, ratio = decode_tolerance_ok(got_bank[sub["k_idx"]], bank_drift[sub["k_idx"]], row_mag, bf16)
+            worst["drift_row"] = max(worst["drift_row"], ratio)
     if len(free_streams):
         assert bits_equal(to_np_bank(bank[free_rows]), bank_free), "final bank differs from the oracle"
     return worst
@@ -321,4 +342,29 @@ def test_full_size_configs(name, free, sync):
     _say(f"{name}: {wl.name}")
     worst = check_decode(wl, 0, free_streams=free, sync_streams=sync, device_inputs=True)
     _say(f"  worst readings {worst['read']:.3g}, rows {worst['row']:.3g} of the bound")
+    torch.cuda.empty_cache()
+
+
+# The largest error of the GPU path run free over a whole sequence against the
+# oracle run free in plain ascending order, as a multiple of the per-step bound,
+# must stay below this many times the sequence length: the errors of two correct
+# summation orders compound from step to step, but stay within a fixed multiple
+# of the per-step bound per step.
+DRIFT_PER_STEP = 1.0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,drift", [
+    ("c1", [2, 512, 1022]),
+    ("c2", [1, 2048, 4094]),
+    ("c4", [1, 299, 510]),
+])
+def test_full_size_free_running_drift(name, drift):
+    """Free-running error growth of the GPU path against the plain ascending order over
+    the whole sequence of c1, c2 and c4 (sampled streams), reported and bounded."""
+    wl = gen.WORKLOADS[name]
+    worst = check_decode(wl, 0, free_streams=[], sync_streams=[], device_inputs=True, drift_streams=drift)
+    _say(f"{name} free-running over {wl.steps} steps against the ascending-order oracle: readings up to "
+         f"{worst['drift_read']:.3g}, written rows up to {worst['drift_row']:.3g} times the per-step bound")
+    assert max(worst["drift_read"], worst["drift_row"]) <= DRIFT_PER_STEP * wl.steps
     torch.cuda.empty_cache()

@@ -8,10 +8,12 @@ own float32 -> bfloat16 conversion (a library routine with that rounding), the
 double path against an exact rational nearest-value search.
 """
 
+import ctypes
 from fractions import Fraction
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from tests.helpers import f32_to_bf16_bits_torch
@@ -124,3 +126,21 @@ def test_nan_with_low_payload_stays_nan_in_the_decode(bits):
                                   np.array([[1.0]], np.float32))
     for b in (int(bank[0, 0]), int(readings[0, 0])):
         assert (b & 0x7f80) == 0x7f80 and (b & 0x007f) != 0, hex(b)
+
+
+def test_array_conversion_is_the_scalar_one():
+    """The oracle's array form converts every element as the scalar form does (edge bit
+    patterns, NaN payloads and random bits), and as torch does on the non-NaN ones."""
+    rng = np.random.default_rng(7)
+    edge = np.array([0, 0x80000000, 1, 0x7fff, 0x8000, 0x8001, 0x18000, 0x3f808000, 0x3f818000, 0x7f7f8000,
+                     0x7f7fffff, 0x7f800000, 0xff800000, 0x7f800001, 0x7fc00000, 0xffffffff, 0x807fffff],
+                     dtype=np.uint32)
+    bits = np.concatenate([edge, rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)])
+    got = oracle.float_to_bf16_array(bits.view(np.float32))
+    lib = oracle._load()
+    want = np.array([lib.oracle_float_to_bf16(ctypes.c_float.from_buffer_copy(int(b).to_bytes(4, "little")))
+                     for b in bits], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    ok = (bits & 0x7fffffff) <= 0x7f800000
+    t = torch.from_numpy(bits[ok].view(np.float32).copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[ok], t)

@@ -126,3 +126,39 @@ def test_worked_float32_ties(name):
     readings = sdm_decode_step(dbank, **{key: t.to(DEV) for key, t in inp.items()})
     assert bits_equal(readings.cpu().numpy(), ref), "readings differ from the oracle"
     assert bits_equal(dbank.cpu().numpy(), ref_bank), "bank differs from the oracle"
+
+
+@pytest.mark.slow
+def test_bf16_conversion_over_every_float32():
+    """The library's float32 -> bfloat16 conversion (sdm_round_bf16, the one every kernel
+    uses on a bfloat16 store) against the oracle's round-to-nearest-even, bit for bit,
+    on all 2^32 float32 bit patterns: 16 batches of 2^28, each generated on the device
+    and on the host from the same counter, the oracle's part split over host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    from sparse_delta_rule_amd import sdm_round_bf16
+
+    batch = 1 << 28
+    threads = 16
+    x = torch.empty(batch, dtype=torch.int32, device=DEV)
+    out = torch.empty(batch, dtype=torch.bfloat16, device=DEV)
+    host = np.empty(batch, dtype=np.uint32)
+    iota = np.arange(batch, dtype=np.uint32)
+    want = np.empty(batch, dtype=np.uint16)
+
+    def ref(i):
+        a, b = batch * i // threads, batch * (i + 1) // threads
+        want[a:b] = oracle.float_to_bf16_array(host[a:b].view(np.float32))
+
+    with ThreadPoolExecutor(threads) as ex:
+        for k in range(16):
+            base = k * batch
+            lo = base - (1 << 32) if base >= 1 << 31 else base  # the same 32 bits as int32
+            x.copy_(torch.arange(lo, lo + batch, dtype=torch.int64, device=DEV))
+            sdm_round_bf16(x.view(torch.float32), out)
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            np.add(iota, np.uint32(base), out=host)
+            list(ex.map(ref, range(threads)))
+            bad = np.flatnonzero(got != want)
+            assert bad.size == 0, (f"batch {k}: {bad.size} differences, first at bits "
+                                   f"{int(host[bad[0]]):#010x}: {int(got[bad[0]]):#06x} vs {int(want[bad[0]]):#06x}")
+            print(f"bfloat16 conversion: bit patterns {base:#010x}..{base + batch - 1:#010x} agree", flush=True)
