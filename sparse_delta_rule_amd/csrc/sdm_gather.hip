@@ -39,6 +39,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kStageEntries = 1024;  // (token, operand) pairs per block x entries per pair staged at once
 constexpr int kNB = 32;              // row loads in flight per lane (a power of two)
+constexpr int kLiveMaxChunks = 4096; // most chunks a launch in the live-token layout scans (per workgroup)
 
 // N consecutive entries [n0, n0 + N) of one operand, all valid: every row load
 // is issued before the first row is used, and each row feeds the sum
@@ -76,8 +77,38 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     }
 }
 
-// NOPS: operands (1 or 2). CMP: compact stash.
-template <typename E, int VB, int NOPS, bool CMP, typename IdxT, typename WT>
+// Live-token layout (LIVE): token block b takes live tokens [b tpb, b tpb + tpb)
+// of the L live tokens in order (chunk by chunk, each chunk's live positions), so
+// every block but the last is full of live tokens, and then writes the outputs
+// (and zero stash rows) of an equal share of the padding tokens; blocks past
+// ceil(L / tpb) (at least one block works) exit at once. Each workgroup finds
+// its tokens from the per-chunk live counts (a scan of chunk_valid in LDS, or
+// the closed form of a scalar valid), its padding share by a binary search of
+// that prefix. Results do not depend on the layout.
+struct LiveMap {
+    const int32_t* pref;  // LDS: pref[c] = live tokens in chunks [0, c), c <= chunks (NULL: scalar valid)
+    int64_t chunks, chunk, v;  // v: live tokens per chunk for a scalar valid
+    __device__ __forceinline__ int64_t before(int64_t c) const { return pref ? int64_t(pref[c]) : c * v; }
+    // token of live index j < before(chunks) for a scalar valid
+    __device__ __forceinline__ int64_t live_token(int64_t j) const {
+        const int64_t c = j / v;
+        return c * chunk + (j - c * v);
+    }
+    // token of padding index j < chunks chunk - before(chunks): in the last chunk c
+    // with c chunk - before(c) <= j (the padding tokens before chunk c)
+    __device__ __forceinline__ int64_t pad_token(int64_t j) const {
+        int64_t lo = 0, hi = chunks - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (mid * chunk - before(mid) <= j) lo = mid; else hi = mid - 1;
+        }
+        const int64_t c = lo;
+        return c * chunk + (before(c + 1) - before(c)) + (j - (c * chunk - before(c)));
+    }
+};
+
+// NOPS: operands (1 or 2). CMP: compact stash. LIVE: live-token layout.
+template <typename E, int VB, int NOPS, bool CMP, bool LIVE, typename IdxT, typename WT>
 __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams p) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
@@ -91,35 +122,108 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const int pair = tid / p.lpr;
     const int g = pair / NOPS;               // token within the block
     const int op = pair - g * NOPS;          // operand
-    // Workgroups are handed to the XCDs in turn (workgroup i to XCD i mod 8): give
-    // XCD x a contiguous share of the (token block, slice) pairs, so chunk positions
-    // (live heads, padding tails) mix evenly over the XCDs.
-    int64_t tblock, slice;
-    {
+    // Workgroups are handed to the XCDs in turn (workgroup i to XCD i mod 8). In the
+    // token order, give XCD x a contiguous share of the (token block, slice) pairs,
+    // so chunk positions (live heads, padding tails) mix evenly over the XCDs; in
+    // the live-token layout, where live blocks come first, keep the hardware's
+    // order, which deals them out to the XCDs in turn.
+    int64_t tblock = blockIdx.x, slice = blockIdx.y;
+    if constexpr (!LIVE) {
         const int64_t n = int64_t(gridDim.x) * gridDim.y, i = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
         const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;
         const int64_t j = x * q + (x < r ? x : r) + k;
         tblock = j % gridDim.x;
         slice = j / gridDim.x;
     }
-    const int64_t t_first = tblock * tpb;
-    const int64_t t = t_first + g;
-    const int vi = int(slice) * p.lpr + lane;
-    const bool lane_on = t < p.tokens && vi < p.vpr;
-    const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
 
     // LDS: slots [op][token][ch], weights [op][token][ch], then (CMP) positions
-    // laid out like the slots (operand 0's part used).
+    // laid out like the slots (operand 0's part used); then (LIVE) the block's
+    // tokens [tpb], the per-chunk prefix [chunks + 1] and the wavefronts' totals.
     IdxT* s_idx = reinterpret_cast<IdxT*>(s_raw);
     WT* s_w = reinterpret_cast<WT*>(s_idx + kStageEntries);
     int32_t* s_kp = reinterpret_cast<int32_t*>(s_w + kStageEntries);
+    int64_t* s_tok = reinterpret_cast<int64_t*>(
+        s_raw + kStageEntries * (sizeof(IdxT) + sizeof(WT) + (CMP ? sizeof(int32_t) : 0)));
+    int32_t* s_pref = reinterpret_cast<int32_t*>(s_tok + kThreads);
 
-    bool live = false;
-    if (t < p.tokens) {
-        const int64_t chunk_no = t / p.chunk;
-        const int64_t limit = p.chunk_valid != nullptr ? int64_t(p.chunk_valid[chunk_no]) : p.valid;
-        live = (t - chunk_no * p.chunk) < limit;
+    int64_t t;          // this thread's token (meaningful when has_tok)
+    bool has_tok, live;
+    LiveMap m;                           // LIVE: the layout
+    int64_t pad_begin = 0, pad_end = 0;  // LIVE: this block's share of the padding tokens
+    if constexpr (LIVE) {
+        m.chunks = p.tokens / p.chunk;
+        m.chunk = p.chunk;
+        m.v = 0;
+        m.pref = nullptr;
+        const int64_t j0 = tblock * tpb;  // this block's first live index
+        if (tid < tpb) s_tok[tid] = 0;    // entries past the live tokens: token 0, whose rows stay unused
+        int64_t live_total;
+        if (p.chunk_valid != nullptr) {
+            // exclusive prefix of the clamped counts: each thread sums a run of chunks,
+            // the runs are scanned within each wavefront (shuffles) and across the
+            // wavefronts (LDS); then each thread fills in its run and places the
+            // block's live tokens that fall in its chunks
+            const int64_t per = (m.chunks + kThreads - 1) / kThreads, c0 = tid * per;
+            int32_t run = 0;
+            for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
+                const int32_t v = p.chunk_valid[c];
+                run += v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
+            }
+            const int wl = tid & 63, wave = tid >> 6;
+            int32_t x = run;
+            for (int d = 1; d < 64; d *= 2) {
+                const int32_t y = __shfl_up(x, d);
+                x += wl >= d ? y : 0;
+            }
+            int32_t* s_wave = s_pref + m.chunks + 1;  // [kThreads / 64] wavefront totals
+            if (wl == 63) s_wave[wave] = x;
+            __syncthreads();  // (also orders the s_tok defaults before the placements below)
+            int32_t acc = x - run;
+            for (int w = 0; w < wave; ++w) acc += s_wave[w];
+            for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
+                s_pref[c] = acc;
+                const int32_t v = p.chunk_valid[c];
+                const int32_t n = v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
+                const int64_t lo = acc > j0 ? acc : j0, hi = acc + n < j0 + tpb ? acc + n : j0 + tpb;
+                for (int64_t j = lo; j < hi; ++j) s_tok[j - j0] = c * p.chunk + (j - acc);
+                acc += n;
+            }
+            int32_t total = 0;
+            for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
+            live_total = total;
+            if (tid == kThreads - 1) s_pref[m.chunks] = total;
+            m.pref = s_pref;
+        } else {
+            m.v = p.valid < p.chunk ? p.valid : p.chunk;
+            live_total = m.before(m.chunks);
+            __syncthreads();  // the s_tok defaults before the placements
+            if (tid < tpb && j0 + tid < live_total) s_tok[tid] = m.live_token(j0 + tid);
+        }
+        const int64_t pads = p.tokens - live_total;
+        const int64_t live_blocks = (live_total + tpb - 1) / tpb;
+        const int64_t workers = live_blocks > 0 ? live_blocks : 1;
+        if (tblock >= workers) return;  // a uniform exit: nothing of this launch is left for this block
+        // the padding tokens are shared out over the blocks that take live tokens
+        const int64_t per_block = (pads + workers - 1) / workers;
+        pad_begin = tblock * per_block < pads ? tblock * per_block : pads;
+        pad_end = pad_begin + per_block < pads ? pad_begin + per_block : pads;
+        __syncthreads();
+        has_tok = j0 + g < live_total;
+        live = has_tok;
+        t = s_tok[g];
+    } else {
+        t = tblock * tpb + g;
+        has_tok = t < p.tokens;
+        live = false;
+        if (has_tok) {
+            const int64_t chunk_no = t / p.chunk;
+            const int64_t limit = p.chunk_valid != nullptr ? int64_t(p.chunk_valid[chunk_no]) : p.valid;
+            live = (t - chunk_no * p.chunk) < limit;
+        }
     }
+    const int vi = int(slice) * p.lpr + lane;
+    const bool lane_on = has_tok && vi < p.vpr;
+    const int64_t col = int64_t(vi < p.vpr ? vi : 0) * VEC;
 
     const E* bank = static_cast<const E*>(p.bank);
     const int width = op == 0 ? p.width0 : p.width1;
@@ -140,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     }
 
     const int wmax = NOPS == 2 && p.width1 > p.width0 ? p.width1 : p.width0;
-    const int64_t t_last = p.tokens - 1;
+    const int64_t t_first = tblock * tpb, t_last = p.tokens - 1;
     for (int base = 0; base < wmax; base += ch) {
         // ---- stage entries [base, base + ch) of every pair of the block: entry k of
         // the staging area is (operand, token, n) = (k / (tpb ch), k / ch % tpb, base + k % ch).
@@ -158,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
                 const int k = tid + r * kThreads;  // within this operand's [tpb][ch]
                 const int tt = k / ch;
                 const int n = min(base + (k - tt * ch), wd - 1);
-                const int64_t tok = min(t_first + tt, t_last);
+                const int64_t tok = LIVE ? s_tok[tt] : min(t_first + tt, t_last);
                 si[o][r] = idx[tok * wd + n];
                 sw[o][r] = w[tok * wd + n];
                 if (CMP && o == 0) sk[r] = p.kpos[tok * wd + n];
@@ -201,36 +305,72 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         }
         if (n < end) gather_batch<E, VB, 1, CMP>(bank, p.hd, col, n, k_base + n, s_idx, s_w, s_kp, stash_row, crow, acc);
     }
-    if (!lane_on) return;
-
-    float* o = out + t * p.hd + col;
-    if (p.out_vec && VEC % 4 == 0) {
+    const auto store_out = [&](int64_t tok) {
+        float* o = out + tok * p.hd + col;
+        if (p.out_vec && VEC % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-            store_stream(reinterpret_cast<float4*>(o + e), make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]));
-    } else {
+            for (int e = 0; e < VEC; e += 4)
+                store_stream(reinterpret_cast<float4*>(o + e), make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]));
+        } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) store_stream(o + e, acc[e]);
+            for (int e = 0; e < VEC; ++e) store_stream(o + e, acc[e]);
+        }
+    };
+    if (lane_on) store_out(t);
+    if constexpr (LIVE) {
+        // this block's share of the padding tokens: +0 outputs and, for a full stash,
+        // zero stash rows, tpb tokens at a time in the same lane layout
+        if (vi >= p.vpr) return;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+        for (int64_t j0 = pad_begin; j0 < pad_end; j0 += tpb) {
+            if (j0 + g >= pad_end) break;
+            const int64_t tp = m.pad_token(j0 + g);
+            store_out(tp);
+            if (!CMP && p.stash != nullptr && op == 0) {
+                E* row = static_cast<E*>(p.stash) + tp * p.width0 * p.hd;
+                V zero;
+                __builtin_memset(&zero, 0, VB);
+                for (int n = 0; n < p.width0; ++n) store_stream(reinterpret_cast<V*>(row + int64_t(n) * p.hd + col), zero);
+            }
+        }
     }
 }
 
-template <typename E, int VB, int NOPS, bool CMP, typename IdxT, typename WT>
+template <typename E, int VB, int NOPS, bool CMP, bool LIVE, typename IdxT, typename WT>
 hipError_t launch_typed(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
-    const int64_t blocks = (p.tokens + geo.tokens_per_block - 1) / geo.tokens_per_block;
+    // the live-token layout may need one more token block (its live and its padding
+    // tokens each end in a partial block)
+    const int64_t blocks = (p.tokens + geo.tokens_per_block - 1) / geo.tokens_per_block + (LIVE ? 1 : 0);
     const dim3 grid(unsigned(blocks), unsigned(geo.slices));
     const dim3 block(kThreads);
-    const size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT) + (CMP ? sizeof(int32_t) : 0));
-    hipLaunchKernelGGL((sdm_gather_kernel<E, VB, NOPS, CMP, IdxT, WT>), grid, block, lds, stream, p);
+    size_t lds = size_t(kStageEntries) * (sizeof(IdxT) + sizeof(WT) + (CMP ? sizeof(int32_t) : 0));
+    if (LIVE) lds += size_t(kThreads) * 8 + (p.chunk_valid ? size_t(p.tokens / p.chunk + 1 + kThreads / 64) * 4 : 0);
+    hipLaunchKernelGGL((sdm_gather_kernel<E, VB, NOPS, CMP, LIVE, IdxT, WT>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 
+template <typename E, int VB, int NOPS, bool CMP, bool LIVE>
+hipError_t launch_live(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
+    if (p.idx64)
+        return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, LIVE, int64_t, uint16_t>(p, geo, stream)
+                        : launch_typed<E, VB, NOPS, CMP, LIVE, int64_t, float>(p, geo, stream);
+    return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, LIVE, int32_t, uint16_t>(p, geo, stream)
+                    : launch_typed<E, VB, NOPS, CMP, LIVE, int32_t, float>(p, geo, stream);
+}
+
+// The live-token layout is used where there is padding to separate (per-chunk
+// counts over at most kLiveMaxChunks chunks, or a scalar valid below the chunk)
+// and no full stash: with a full stash, padding tokens write whole zero stash
+// rows, work the token order already spreads over the launch (measured: the
+// live-token layout gains nothing there).
 template <typename E, int VB, int NOPS, bool CMP>
 hipError_t launch_ops(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
-    if (p.idx64)
-        return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, int64_t, uint16_t>(p, geo, stream)
-                        : launch_typed<E, VB, NOPS, CMP, int64_t, float>(p, geo, stream);
-    return p.w_bf16 ? launch_typed<E, VB, NOPS, CMP, int32_t, uint16_t>(p, geo, stream)
-                    : launch_typed<E, VB, NOPS, CMP, int32_t, float>(p, geo, stream);
+    const bool full_stash = p.stash != nullptr && !CMP;
+    const bool live = !full_stash && (p.chunk_valid != nullptr ? p.tokens / p.chunk <= kLiveMaxChunks
+                                                                : p.valid < p.chunk);
+    return live ? launch_live<E, VB, NOPS, CMP, true>(p, geo, stream)
+                : launch_live<E, VB, NOPS, CMP, false>(p, geo, stream);
 }
 
 template <typename E, int VB>
