@@ -127,6 +127,59 @@ def _stream_handle(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# The per-row arrays of sdm_decode_step / sdm_decode_steps in their C argument
+# order, each with the width of its last axis in terms of the call's sizes.
+_DECODE_ROWS = (("k_idx", "W"), ("k_val", "W"), ("v", "head_dim"), ("q_val", "R"), ("beta", "one"),
+                ("g", "G"), ("q_idx", "R"))
+
+
+def _decode_marshal(bank, tensors: dict, readings, first_axis_is_steps: bool):
+    """Checks of the torch side of a decode call and the C call's sizes: every per-row
+    array is [rows..., width] with the same leading axes, its width as _DECODE_ROWS
+    states; readings is shaped like v in the bank dtype (allocated when None).
+    Returns (readings, sizes) with sizes the C ABI's head_dim, steps, streams, W, R, G."""
+    if bank.dim() != 2:
+        raise ValueError("bank must be [num_slots, head_dim]")
+    lead = tuple(tensors["k_idx"].shape[:-1])
+    if first_axis_is_steps and len(lead) < 1:
+        raise ValueError("k_idx must be [steps, ..., W]")
+    sizes = {"head_dim": bank.shape[1], "one": 1, "W": tensors["k_idx"].shape[-1],
+             "R": tensors["q_idx"].shape[-1], "G": tensors["g"].shape[-1]}
+    for name, width in _DECODE_ROWS:
+        shape = tuple(tensors[name].shape)
+        if shape[:-1] != lead or shape[-1:] != (sizes[width],):
+            raise ValueError(f"{name} has shape {shape}; the call needs {lead + (sizes[width],)} "
+                             f"(leading axes of k_idx, last axis {width})")
+    if not (tensors["k_val"].dtype == tensors["v"].dtype == tensors["q_val"].dtype):
+        raise TypeError("k_val, v and q_val must share one dtype")
+    if tensors["beta"].dtype != torch.float32 or tensors["g"].dtype != torch.float32:
+        raise TypeError("beta and g must be float32")
+    v = tensors["v"]
+    if readings is None:
+        readings = torch.empty(v.shape, dtype=bank.dtype, device=bank.device)
+    elif tuple(readings.shape) != tuple(v.shape) or readings.dtype != bank.dtype:
+        raise ValueError("readings must be shaped like v, in the bank dtype")
+    _dev_check(bank.device, bank=bank, readings=readings, **tensors)
+    rows = 1
+    for n in lead:
+        rows *= n
+    steps = lead[0] if first_axis_is_steps else 1
+    streams = rows // steps if steps else 0
+    return readings, (sizes["head_dim"], steps, streams, sizes["W"], sizes["R"], sizes["G"])
+
+
+def _decode_call(fn, bank, t, readings, sizes):
+    hd, steps, streams, W, R, G = sizes
+    head = (_ptr(bank), _dt(bank, "bank"), bank.shape[0], hd) + ((steps,) if fn == "sdm_decode_steps" else ())
+    rc = getattr(library(), fn)(
+        *head, streams, W, R, G, _ptr(t["k_idx"]), _dt(t["k_idx"], "k_idx"), _ptr(t["k_val"]), _ptr(t["v"]),
+        _ptr(t["q_val"]), _dt(t["v"], "v"), _ptr(t["beta"]), _ptr(t["g"]), _ptr(t["q_idx"]),
+        _dt(t["q_idx"], "q_idx"), _ptr(readings), _stream_handle(bank.device))
+    if rc != 0:
+        _raise(rc)
+    return readings
+
+
 def sdm_decode_step(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
                     beta: torch.Tensor, g: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor,
                     readings: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -138,34 +191,9 @@ def sdm_decode_step(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor
     k_val, v and q_val share one dtype (float32 or bfloat16); beta and g are float32.
     Returns readings shaped like ``v`` in the bank dtype (``readings`` if given).
     """
-    if bank.dim() != 2:
-        raise ValueError("bank must be [num_slots, head_dim]")
-    hd = bank.shape[1]
-    W, R, G = k_idx.shape[-1], q_idx.shape[-1], g.shape[-1]
-    lead = tuple(k_idx.shape[:-1])
-    for name, t, n in (("k_val", k_val, W), ("v", v, hd), ("beta", beta, 1), ("g", g, G),
-                       ("q_idx", q_idx, R), ("q_val", q_val, R)):
-        if tuple(t.shape) != lead + (n,):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {lead + (n,)}")
-    if not (k_val.dtype == v.dtype == q_val.dtype):
-        raise TypeError("k_val, v and q_val must share one dtype")
-    if beta.dtype != torch.float32 or g.dtype != torch.float32:
-        raise TypeError("beta and g must be float32")
-    if readings is None:
-        readings = torch.empty(v.shape, dtype=bank.dtype, device=bank.device)
-    elif tuple(readings.shape) != tuple(v.shape) or readings.dtype != bank.dtype:
-        raise ValueError("readings must be shaped like v, in the bank dtype")
-    _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
-               q_val=q_val, readings=readings)
-    streams = k_idx.numel() // W if W else 0  # W = 0 is left to the library to reject
-    rc = library().sdm_decode_step(
-        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, streams, W, R, G,
-        _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
-        _ptr(beta), _ptr(g), _ptr(q_idx), _dt(q_idx, "q_idx"), _ptr(readings),
-        _stream_handle(bank.device))
-    if rc != 0:
-        _raise(rc)
-    return readings
+    t = dict(k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx, q_val=q_val)
+    readings, sizes = _decode_marshal(bank, t, readings, first_axis_is_steps=False)
+    return _decode_call("sdm_decode_step", bank, t, readings, sizes)
 
 
 def sdm_decode_steps(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
@@ -179,35 +207,9 @@ def sdm_decode_steps(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tenso
     applied before token t + 1; the result equals ``steps`` single-step calls.
     Returns readings shaped like ``v`` in the bank dtype.
     """
-    if bank.dim() != 2 or k_idx.dim() < 2:
-        raise ValueError("bank must be [num_slots, head_dim] and k_idx [steps, ..., W]")
-    hd = bank.shape[1]
-    W, R, G = k_idx.shape[-1], q_idx.shape[-1], g.shape[-1]
-    lead = tuple(k_idx.shape[:-1])
-    for name, t, n in (("k_val", k_val, W), ("v", v, hd), ("beta", beta, 1), ("g", g, G),
-                       ("q_idx", q_idx, R), ("q_val", q_val, R)):
-        if tuple(t.shape) != lead + (n,):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {lead + (n,)}")
-    if not (k_val.dtype == v.dtype == q_val.dtype):
-        raise TypeError("k_val, v and q_val must share one dtype")
-    if beta.dtype != torch.float32 or g.dtype != torch.float32:
-        raise TypeError("beta and g must be float32")
-    if readings is None:
-        readings = torch.empty(v.shape, dtype=bank.dtype, device=bank.device)
-    elif tuple(readings.shape) != tuple(v.shape) or readings.dtype != bank.dtype:
-        raise ValueError("readings must be shaped like v, in the bank dtype")
-    _dev_check(bank.device, bank=bank, k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx,
-               q_val=q_val, readings=readings)
-    steps = lead[0]
-    streams = k_idx.numel() // (W * steps) if W and steps else 0  # W = 0: rejected by the library
-    rc = library().sdm_decode_steps(
-        _ptr(bank), _dt(bank, "bank"), bank.shape[0], hd, steps, streams, W, R, G,
-        _ptr(k_idx), _dt(k_idx, "k_idx"), _ptr(k_val), _ptr(v), _ptr(q_val), _dt(v, "v"),
-        _ptr(beta), _ptr(g), _ptr(q_idx), _dt(q_idx, "q_idx"), _ptr(readings),
-        _stream_handle(bank.device))
-    if rc != 0:
-        _raise(rc)
-    return readings
+    t = dict(k_idx=k_idx, k_val=k_val, v=v, beta=beta, g=g, q_idx=q_idx, q_val=q_val)
+    readings, sizes = _decode_marshal(bank, t, readings, first_axis_is_steps=True)
+    return _decode_call("sdm_decode_steps", bank, t, readings, sizes)
 
 
 def _gather_operands(bank, idx0, w0, chunk, valid, chunk_valid, idx1, w1, out0, out1, stash, stash_shape,

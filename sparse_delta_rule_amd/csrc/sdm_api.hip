@@ -297,12 +297,12 @@ int decode_call(const char* fn, void* bank, int bank_dtype, int64_t num_slots, i
         return fail(SDM_E_DTYPE, "%s: k_idx and q_idx must be int32 or int64 (dtypes %d, %d)", fn, k_idx_dtype,
                     q_idx_dtype);
     if (num_slots < 1 || head_dim < 1)
-        return fail(SDM_E_SHAPE, "%s: the bank needs at least one slot and one column, got [%lld, %lld]", fn,
+        return fail(SDM_E_SHAPE, "%s: empty bank [%lld, %lld]: num_slots and head_dim must both be positive", fn,
                     (long long)num_slots, (long long)head_dim);
     if (streams < 0) return fail(SDM_E_SHAPE, "%s: streams = %lld < 0", fn, (long long)streams);
     if (steps < 0) return fail(SDM_E_SHAPE, "%s: steps = %lld < 0", fn, (long long)steps);
     if (W < 1 || W > SDM_MAX_WIDTH || R < 1 || R > SDM_MAX_WIDTH)
-        return fail(SDM_E_RANGE, "%s: W and R must be in 1..%d, got W=%d, R=%d", fn, SDM_MAX_WIDTH, W, R);
+        return fail(SDM_E_RANGE, "%s: W=%d, R=%d: each width must lie in 1..%d", fn, W, R, SDM_MAX_WIDTH);
     if (G != 1 && G != W) return fail(SDM_E_SHAPE, "%s: G must be 1 or W=%d, got %d", fn, W, G);
     const int es = elem_size(bank_dtype);
     if (!mul_fits(num_slots, head_dim, es) || !mul_fits(steps, streams, head_dim * es) ||
@@ -421,17 +421,17 @@ int gather_prepare(const char* fn, const void* bank, int bank_dtype, int64_t num
     if (w_dtype != SDM_F32 && w_dtype != SDM_BF16)
         return fail(SDM_E_DTYPE, "%s: weights must be float32 or bfloat16 (dtype %d)", fn, w_dtype);
     if (num_slots < 1 || head_dim < 1)
-        return fail(SDM_E_SHAPE, "%s: the bank needs at least one slot and one column, got [%lld, %lld]", fn,
+        return fail(SDM_E_SHAPE, "%s: empty bank [%lld, %lld]: num_slots and head_dim must both be positive", fn,
                     (long long)num_slots, (long long)head_dim);
     if (tokens < 0 || chunk < 1 || tokens % chunk != 0 || valid < 0 || valid > chunk)
-        return fail(SDM_E_SHAPE, "%s: need tokens = k * chunk and 0 <= valid <= chunk, got tokens=%lld "
+        return fail(SDM_E_SHAPE, "%s: tokens must be a whole number of chunks and valid lie in [0, chunk]: tokens=%lld "
                     "chunk=%lld valid=%lld", fn, (long long)tokens, (long long)chunk, (long long)valid);
     if (width0 < 1 || width0 > SDM_MAX_WIDTH)
         return fail(SDM_E_RANGE, "%s: width0 must be in 1..%d, got %d", fn, SDM_MAX_WIDTH, width0);
     const bool two = idx1 != nullptr || w1 != nullptr || out1 != nullptr || width1 != 0;
     if (two) {
         if (idx1 == nullptr || w1 == nullptr || out1 == nullptr)
-            return fail(SDM_E_NULL, "%s: idx1, w1 and out1 go together", fn);
+            return fail(SDM_E_NULL, "%s: operand 1 is given in part: pass idx1, w1 and out1 all, or none", fn);
         if (width1 < 1 || width1 > SDM_MAX_WIDTH)
             return fail(SDM_E_RANGE, "%s: width1 must be in 1..%d, got %d", fn, SDM_MAX_WIDTH, width1);
     }
@@ -452,10 +452,10 @@ int gather_prepare(const char* fn, const void* bank, int bank_dtype, int64_t num
     const int64_t stash_bytes = stash != nullptr ? tokens * width0 * head_dim * es : 0;
     if (overlap(out0, out_bytes, bank, bank_bytes) || overlap(stash, stash_bytes, bank, bank_bytes) ||
         (two && overlap(out1, out_bytes, bank, bank_bytes)))
-        return fail(SDM_E_OVERLAP, "%s: stash and outputs must not overlap the bank", fn);
+        return fail(SDM_E_OVERLAP, "%s: the stash or an output shares memory with the bank", fn);
     if (overlap(out0, out_bytes, stash, stash_bytes) || (two && (overlap(out1, out_bytes, stash, stash_bytes) ||
                                                                  overlap(out0, out_bytes, out1, out_bytes))))
-        return fail(SDM_E_OVERLAP, "%s: stash and outputs must not overlap one another", fn);
+        return fail(SDM_E_OVERLAP, "%s: the stash and the outputs share memory", fn);
 
     if (debug_validate()) {
         const void* ptrs[] = {bank, idx0, w0, out0, stash, chunk_valid, kpos, idx1, w1, out1};

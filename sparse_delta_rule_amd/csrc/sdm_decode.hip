@@ -278,8 +278,10 @@ __device__ __forceinline__ void load_held_rows(typename RawVec<VB>::T (&row)[JN]
     for (int j = 0; j < JN; ++j) row[j] = *reinterpret_cast<const V*>(bank + h.slot[j] * hd + ln.vcol);
 }
 
-// Decay-and-write of the W rows this lane holds. Write slots are distinct within
-// a stream, so plain stores suffice. opaque() hides the raw bits from the
+// Decay-and-write of the W rows this lane holds. No two of a stream's writes go
+// to one slot (a precondition of the call), and no other workgroup writes these
+// columns of these slots, so each element is stored once, with an ordinary
+// store, and no atomics are needed. opaque() hides the raw bits from the
 // optimiser, so the rows are widened again here instead of being kept widened
 // (twice the registers for bfloat16) across the barriers before this point.
 template <typename E, int VB, int JN, typename RowMeta>

@@ -55,11 +55,10 @@ __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint
 __device__ __forceinline__ float widen(float f) { return f; }
 
 // float32 -> bfloat16 bits, round to nearest even, NaN kept a NaN with its quiet
-// bit set: gfx950's packed conversion (two values per instruction). Its result
-// equals the bit-level definition (add 0x7fff plus the kept half's lowest bit,
-// keep the high half; for a NaN, the high half with the quiet bit set) for every
-// one of the 2^32 float32 inputs, denormals included, at this library's default
-// floating-point mode.
+// bit set: gfx950's packed conversion (two values per instruction). sdm_round_bf16
+// exposes it, and a GPU test compares it, bit for bit, with the oracle's
+// bit-level rounding on every one of the 2^32 float32 inputs (denormals and NaN
+// payloads included).
 typedef __bf16 Bf16x2 __attribute__((ext_vector_type(2)));
 typedef float F32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t to_bf16x2_rne(float lo, float hi) {

@@ -97,13 +97,13 @@ def call_decode(**kw):
     (dict(val_dtype=I64), E_DTYPE, "k_val, v, q_val"),
     (dict(k_idx_dtype=F32), E_DTYPE, "k_idx and q_idx"),
     (dict(q_idx_dtype=BF16), E_DTYPE, "k_idx and q_idx"),
-    (dict(num_slots=0), E_SHAPE, "at least one slot"),
-    (dict(head_dim=0), E_SHAPE, "at least one slot"),
+    (dict(num_slots=0), E_SHAPE, "empty bank"),
+    (dict(head_dim=0), E_SHAPE, "empty bank"),
     (dict(streams=-1), E_SHAPE, "streams"),
-    (dict(W=0), E_RANGE, "W and R"),
-    (dict(W=257), E_RANGE, "W and R"),
-    (dict(R=0), E_RANGE, "W and R"),
-    (dict(R=300), E_RANGE, "W and R"),
+    (dict(W=0), E_RANGE, "each width must lie in 1..256"),
+    (dict(W=257), E_RANGE, "each width must lie in 1..256"),
+    (dict(R=0), E_RANGE, "each width must lie in 1..256"),
+    (dict(R=300), E_RANGE, "each width must lie in 1..256"),
     (dict(G=2), E_SHAPE, "G must be 1 or W"),
     (dict(W=4, G=5), E_SHAPE, "G must be 1 or W"),
     (dict(bank=None), E_NULL, "bank is NULL"),
@@ -141,7 +141,7 @@ def call_decode_steps(steps, **kw):
 
 @pytest.mark.parametrize("steps,kw,code,text", [
     (-1, {}, E_SHAPE, "steps = -1"),
-    (4, dict(W=0), E_RANGE, "W and R"),
+    (4, dict(W=0), E_RANGE, "each width must lie in 1..256"),
     (4, dict(G=3), E_SHAPE, "G must be 1 or W"),
     (4, dict(v=None), E_NULL, "v is NULL"),
     (4, dict(q_val=A + 1300 * MB + 2, val_dtype=F32), E_ALIGN, "aligned"),
@@ -191,30 +191,30 @@ def call_gather(**kw):
     (dict(bank_dtype=I64), E_DTYPE, "bank must be"),
     (dict(idx_dtype=F32), E_DTYPE, "indices must be"),
     (dict(w_dtype=I32), E_DTYPE, "weights must be"),
-    (dict(num_slots=0), E_SHAPE, "at least one slot"),
-    (dict(head_dim=0), E_SHAPE, "at least one slot"),
-    (dict(tokens=-16), E_SHAPE, "tokens = k * chunk"),
-    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
-    (dict(chunk=0), E_SHAPE, "tokens = k * chunk"),
-    (dict(valid=17), E_SHAPE, "valid <= chunk"),
-    (dict(valid=-1), E_SHAPE, "valid <= chunk"),
+    (dict(num_slots=0), E_SHAPE, "empty bank"),
+    (dict(head_dim=0), E_SHAPE, "empty bank"),
+    (dict(tokens=-16), E_SHAPE, "whole number of chunks"),
+    (dict(tokens=60), E_SHAPE, "whole number of chunks"),
+    (dict(chunk=0), E_SHAPE, "whole number of chunks"),
+    (dict(valid=17), E_SHAPE, "valid lie in [0, chunk]"),
+    (dict(valid=-1), E_SHAPE, "valid lie in [0, chunk]"),
     (dict(width0=0), E_RANGE, "width0"),
     (dict(width0=257), E_RANGE, "width0"),
     (dict(width1=0), E_RANGE, "width1"),
     (dict(width1=257), E_RANGE, "width1"),
-    (dict(idx1=None), E_NULL, "go together"),
-    (dict(out1=None), E_NULL, "go together"),
-    (dict(idx1=None, w1=None, out1=None, width1=3), E_NULL, "go together"),
+    (dict(idx1=None), E_NULL, "given in part"),
+    (dict(out1=None), E_NULL, "given in part"),
+    (dict(idx1=None, w1=None, out1=None, width1=3), E_NULL, "given in part"),
     (dict(bank=None), E_NULL, "required"),
     (dict(out0=None), E_NULL, "required"),
     (dict(bank=A + 2, bank_dtype=F32), E_ALIGN, "aligned"),
     (dict(out0=A + 1200 * MB + 2), E_ALIGN, "aligned"),
     (dict(chunk_valid=A + 1700 * MB + 1), E_ALIGN, "aligned"),
-    (dict(out0=A + 1000 * 128), E_OVERLAP, "overlap the bank"),
-    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "overlap the bank"),
-    (dict(out1=A + 128), E_OVERLAP, "overlap the bank"),
-    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
-    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+    (dict(out0=A + 1000 * 128), E_OVERLAP, "shares memory with the bank"),
+    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "shares memory with the bank"),
+    (dict(out1=A + 128), E_OVERLAP, "shares memory with the bank"),
+    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "the stash and the outputs share memory"),
+    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "the stash and the outputs share memory"),
 ])
 def test_gather_rejects(kw, code, text):
     rc, msg = call_gather(**kw)
@@ -241,10 +241,10 @@ def call_gather_compact(kpos=A + 1800 * MB, **kw):
     (dict(stash=None), E_NULL, "stash and kpos are required"),
     (dict(kpos=None), E_NULL, "stash and kpos are required"),
     (dict(kpos=A + 1800 * MB + 2), E_ALIGN, "aligned"),
-    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
+    (dict(tokens=60), E_SHAPE, "whole number of chunks"),
     (dict(width0=0), E_RANGE, "width0"),
-    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
-    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "overlap the bank"),
+    (dict(stash=A + 1200 * MB + 4096), E_OVERLAP, "the stash and the outputs share memory"),
+    (dict(stash=A - 64 * 8 * 128 * 2 + 2), E_OVERLAP, "shares memory with the bank"),
 ])
 def test_gather_compact_rejects(kw, code, text):
     rc, msg = call_gather_compact(**kw)
@@ -281,11 +281,11 @@ def plan_launch(plan, row0, valid):
     (dict(row0_max=-1), E_SHAPE, "row0_max = -1"),
     (dict(row0_max=(1 << 63) - 10), E_SHAPE, "overflows"),
     (dict(bank_dtype=I64), E_DTYPE, "bank must be"),
-    (dict(tokens=60), E_SHAPE, "tokens = k * chunk"),
+    (dict(tokens=60), E_SHAPE, "whole number of chunks"),
     (dict(width0=0), E_RANGE, "width0"),
-    (dict(idx1=None), E_NULL, "go together"),
-    (dict(out0=A + 1000 * 128), E_OVERLAP, "overlap the bank"),
-    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "one another"),
+    (dict(idx1=None), E_NULL, "given in part"),
+    (dict(out0=A + 1000 * 128), E_OVERLAP, "shares memory with the bank"),
+    (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "the stash and the outputs share memory"),
 ])
 def test_gather_plan_init_rejects(kw, code, text):
     plan = Plan()
@@ -373,3 +373,46 @@ def test_python_binding_checks_the_extent_of_given_outputs():
         sdm.sdm_gather(bank, idx, w, chunk=3, chunk_valid=torch.zeros(3, dtype=torch.int32))
     with pytest.raises(ValueError, match="is on cpu"):  # right extents: on to the device check
         sdm.sdm_gather(bank, idx, w, chunk=3, chunk_valid=torch.zeros(2, dtype=torch.int32))
+
+
+# ------------------------------------------------------------ python binding checks
+def _decode_tensors(S=3, W=4, R=5, G=1, hd=8, steps=None):
+    import torch
+    lead = (S,) if steps is None else (steps, S)
+    return dict(k_idx=torch.zeros(lead + (W,), dtype=torch.int64), k_val=torch.zeros(lead + (W,)),
+                v=torch.zeros(lead + (hd,)), beta=torch.zeros(lead + (1,)), g=torch.zeros(lead + (G,)),
+                q_idx=torch.zeros(lead + (R,), dtype=torch.int64), q_val=torch.zeros(lead + (R,)))
+
+
+@pytest.mark.parametrize("name,shape", [("k_val", (3, 5)), ("v", (3, 7)), ("beta", (3, 2)), ("q_val", (3, 4)),
+                                        ("q_idx", (2, 5)), ("g", (4, 1))])
+def test_binding_rejects_misshaped_decode_rows(name, shape):
+    import torch
+    t = _decode_tensors()
+    t[name] = torch.zeros(shape, dtype=t[name].dtype)
+    with pytest.raises(ValueError, match=f"{name} has shape"):
+        sdm.sdm_decode_step(torch.zeros(64, 8), **t)
+
+
+def test_binding_rejects_decode_dtypes_and_readings():
+    import torch
+    t = _decode_tensors()
+    t["v"] = t["v"].to(torch.bfloat16)
+    with pytest.raises(TypeError, match="share one dtype"):
+        sdm.sdm_decode_step(torch.zeros(64, 8), **t)
+    t = _decode_tensors()
+    t["g"] = t["g"].double()
+    with pytest.raises(TypeError, match="float32"):
+        sdm.sdm_decode_step(torch.zeros(64, 8), **t)
+    with pytest.raises(ValueError, match="readings"):
+        sdm.sdm_decode_step(torch.zeros(64, 8), **_decode_tensors(), readings=torch.zeros(3, 9))
+    with pytest.raises(ValueError, match="bank must be"):
+        sdm.sdm_decode_step(torch.zeros(64), **_decode_tensors())
+    # the multi-token form wants the token axis first on every row array
+    t = _decode_tensors(steps=2)
+    t["beta"] = torch.zeros(3, 1)
+    with pytest.raises(ValueError, match="beta has shape"):
+        sdm.sdm_decode_steps(torch.zeros(64, 8), **t)
+    # on the CPU the shapes pass and the device check refuses
+    with pytest.raises(ValueError, match="is on cpu"):
+        sdm.sdm_decode_steps(torch.zeros(64, 8), **_decode_tensors(steps=2))
