@@ -145,6 +145,11 @@ def parse_args(argv=None):
                         "streams: each run of 64 units draws its rows from its own range of 16384 slots")
     p.add_argument("--ingest-ceiling", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="summarise rocprofv3 output of one --ceiling run (one bank size) into profiles/ (no GPU)")
+    p.add_argument("--tokens", type=int, default=None,
+                   help="gather: launch over this many tokens (a multiple of the chunk) instead of the workload's")
+    p.add_argument("--valid", default="per-chunk",
+                   help="gather: per-chunk (the workload's per-chunk counts), all (every token live, no counts) "
+                        "or N (one count N for every chunk, passed as the scalar valid)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -490,10 +495,22 @@ def bench_gather(torch, args, cfg_name, wl):
     from sparse_delta_rule_amd import sdm_gather, sdm_gather_compact
     dev = torch.device("cuda", 0)
     es = torch.empty((), dtype=wl.bank_dtype).element_size()
+    if args.tokens is not None:
+        if args.tokens < wl.chunk or args.tokens % wl.chunk:
+            raise SystemExit("bench.py: --tokens must be a positive multiple of the chunk")
+        wl = wl.replace(tokens=args.tokens)
     bank = gen.gather_bank(wl, args.seed, dev)
     inp = gen.gather_inputs(wl, args.seed, dev)
     T = wl.tokens
-    live = gen.live_tokens(wl, inp["chunk_valid"])
+    # padding: the workload's per-chunk counts, or one scalar count for every chunk
+    if args.valid == "per-chunk":
+        cv, valid = inp["chunk_valid"], wl.chunk
+        live = gen.live_tokens(wl, cv)
+    else:
+        cv, valid = None, wl.chunk if args.valid == "all" else int(args.valid)
+        if not 0 <= valid <= wl.chunk:
+            raise SystemExit("bench.py: --valid must be per-chunk, all or a count in [0, chunk]")
+        live = T // wl.chunk * valid
     two = args.gather in ("two-ops", "no-stash", "compact")
     with_stash = args.gather in ("two-ops", "one-op")
     compact = args.gather == "compact"
@@ -501,7 +518,8 @@ def bench_gather(torch, args, cfg_name, wl):
     out1 = torch.empty((T, wl.head_dim), device=dev) if two else None
     stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev) if with_stash else None
     if compact:
-        kpos = gen.compact_positions(inp["idx0"], wl.chunk, inp["chunk_valid"])
+        kpos = gen.compact_positions(inp["idx0"], wl.chunk,
+                                     cv if cv is not None else torch.full((T // wl.chunk,), valid, device=dev))
         chunk_of = (torch.arange(T, device=dev) // wl.chunk)[:, None].expand_as(kpos)
         stored = kpos >= 0
         # rows the compact stash must hold: distinct (chunk, position) pairs
@@ -509,17 +527,17 @@ def bench_gather(torch, args, cfg_name, wl):
         stash = torch.empty((T // wl.chunk, wl.chunk * wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev)
     torch.cuda.synchronize()
     cpu = None
-    if not args.no_cpu_baseline and args.gather == "two-ops":
+    if not args.no_cpu_baseline and args.gather == "two-ops" and args.valid == "per-chunk":
         cpu = cpu_baseline_gather(torch, wl, bank, inp, args.cpu_seconds, cfg_name)
     K = args.steps if args.steps is not None else 20
     ops = dict(idx1=inp["idx1"], w1=inp["w1"], out1=out1) if two else {}
 
     def launch_one(i):
         if compact:
-            sdm_gather_compact(bank, inp["idx0"], inp["w0"], kpos, chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+            sdm_gather_compact(bank, inp["idx0"], inp["w0"], kpos, chunk=wl.chunk, valid=valid, chunk_valid=cv,
                                out0=out0, stash=stash, **ops)
         else:
-            sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"], out0=out0,
+            sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, valid=valid, chunk_valid=cv, out0=out0,
                        stash=stash, with_stash=with_stash, **ops)
 
     ms = _run_steps(torch, args, launch_one, K)
@@ -529,7 +547,9 @@ def bench_gather(torch, args, cfg_name, wl):
     row_bytes = (live * width_read + stash_rows) * wl.head_dim * es
     gbps = row_bytes / (ms_step * 1e-3) / 1e9
     name = f"{cfg_name}: {wl.name}" + ("" if args.gather == "two-ops" else f" [{args.gather}]")
-    config = {"workload": name, "tokens": T, "live_tokens": live, "chunk": wl.chunk,
+    if args.tokens is not None or args.valid != "per-chunk":
+        name += f" [{T} tokens, valid {args.valid}]"
+    config = {"workload": name, "tokens": T, "live_tokens": live, "valid": args.valid, "chunk": wl.chunk,
               "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0],
               "stash": "compact" if compact else with_stash, "stash_rows": stash_rows,
               "slots": wl.num_slots, "bank_dtype": str(wl.bank_dtype).replace("torch.", ""),
