@@ -143,6 +143,9 @@ def parse_args(argv=None):
     p.add_argument("--ceiling-layout", default="uniform", choices=["uniform", "streams"],
                    help="with --ceiling: rows uniform over the bank, or (rmw, mix) laid out as the decode's c2 "
                         "streams: each run of 64 units draws its rows from its own range of 16384 slots")
+    p.add_argument("--host-call-cost", action="store_true",
+                   help="host time per call of a small gather (64 tokens, two operands, no stash), launched "
+                        "back to back: sdm_gather and a gather plan's launch, from Python and through ctypes")
     p.add_argument("--ingest-ceiling", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="summarise rocprofv3 output of one --ceiling run (one bank size) into profiles/ (no GPU)")
     p.add_argument("--tokens", type=int, default=None,
@@ -714,6 +717,55 @@ def bench_ceiling(torch, args) -> int:
     return 0
 
 
+def host_call_cost(torch, calls: int = 2000) -> int:
+    """Host time per call, in microseconds, of a 64-token two-operand gather (no stash)
+    over c3's bank: sdm_gather from Python, the same C call through ctypes with its
+    arguments prepared once, a plan launch from Python and through ctypes. The device
+    work is the same for all four; this measures what a call costs the host."""
+    import ctypes
+    import gen
+    from sparse_delta_rule_amd import sdm_gather, sdm_gather_plan, library
+    from sparse_delta_rule_amd._binding import _stream_handle
+    dev = torch.device("cuda", 0)
+    wl = gen.WORKLOADS["c3"].replace(num_slots=1 << 20, tokens=64)
+    bank = gen.gather_bank(wl, 0, dev)
+    inp = gen.gather_inputs(wl, 0, dev)
+    out0 = torch.empty((64, wl.head_dim), device=dev)
+    out1 = torch.empty_like(out0)
+    lib = library()
+    stream = _stream_handle(dev)
+    P = ctypes.c_void_p
+    args = (P(bank.data_ptr()), 1, bank.shape[0], wl.head_dim, 64, 64, 64, None, 2, 1,
+            P(inp["idx0"].data_ptr()), P(inp["w0"].data_ptr()), 64, P(out0.data_ptr()), None,
+            P(inp["idx1"].data_ptr()), P(inp["w1"].data_ptr()), 64, P(out1.data_ptr()), stream)
+    plan = sdm_gather_plan(bank, inp["idx0"], inp["w0"], tokens=64, chunk=64, idx1=inp["idx1"], w1=inp["w1"],
+                           out0=out0, out1=out1)
+    pl = ctypes.byref(plan._plan)
+    ways = {
+        "sdm_gather (Python)": lambda: sdm_gather(bank, inp["idx0"], inp["w0"], chunk=64, valid=64, idx1=inp["idx1"],
+                                                  w1=inp["w1"], out0=out0, out1=out1, with_stash=False),
+        "sdm_gather (ctypes)": lambda: lib.sdm_gather(*args),
+        "plan launch (Python)": lambda: plan.launch(0, 64),
+        "plan launch (ctypes)": lambda: lib.sdm_gather_plan_launch(pl, 0, 64, stream),
+    }
+    if lib.sdm_gather(*args) != 0 or lib.sdm_gather_plan_launch(pl, 0, 64, stream) != 0:
+        raise SystemExit(f"bench.py: a gather call failed: {lib.sdm_last_error().decode()}")
+    out = {}
+    for name, call in ways.items():
+        for _ in range(50):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            call()
+        host = (time.perf_counter() - t0) / calls * 1e6
+        torch.cuda.synchronize()
+        out[name] = host
+    print(json.dumps({"metric": "host time per call, us (64-token two-operand gather, no stash)",
+                      "calls": calls, **{k: round(v, 2) for k, v in out.items()}}), flush=True)
+    return 0
+
+
 # ------------------------------------------------------------------ profiles
 def _csv_rows(directory: str, suffix: str):
     import csv
@@ -1031,6 +1083,8 @@ def main(argv=None):
         return 0
     if args.ceiling:
         return bench_ceiling(torch, args)
+    if args.host_call_cost:
+        return host_call_cost(torch)
     import gen
     wl = gen.WORKLOADS[args.config]
     if args.streams is not None:
