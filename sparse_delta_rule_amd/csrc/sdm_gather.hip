@@ -29,6 +29,12 @@
 // slots and weights, and a live entry with a position p >= 0 stores its row at
 // row p of its chunk's block of chunk * width0 rows instead of at (t, n); other
 // entries and padding tokens store nothing.
+//
+// Launches without a stash whose rows are 16 lane-vectors wide take the pair
+// layout instead (sdm_gather_pair_kernel, described where it is defined): no
+// LDS staging, the slots passed round a 16-lane group by DPP row broadcasts, few
+// registers and so more wavefronts in flight. Which layout runs changes no bit
+// of any result.
 
 #include "sdm_kernels.h"
 
@@ -93,6 +99,16 @@ struct LiveMap {
     __device__ __forceinline__ int64_t live_token(int64_t j) const {
         const int64_t c = j / v;
         return c * chunk + (j - c * v);
+    }
+    // token of live index j < before(chunks): in the last chunk c with before(c) <= j
+    __device__ __forceinline__ int64_t live_at(int64_t j) const {
+        if (pref == nullptr) return live_token(j);
+        int64_t lo = 0, hi = chunks - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (before(mid) <= j) lo = mid; else hi = mid - 1;
+        }
+        return lo * chunk + (j - before(lo));
     }
     // token of padding index j < chunks chunk - before(chunks): in the last chunk c
     // with c chunk - before(c) <= j (the padding tokens before chunk c)
@@ -167,7 +183,9 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
             int32_t run = 0;
             for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
                 const int32_t v = p.chunk_valid[c];
-                run += v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
+                const int32_t n = v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
+                s_pref[c] = n;  // the clamped count, until this thread's pass below
+                run += n;
             }
             const int wl = tid & 63, wave = tid >> 6;
             int32_t x = run;
@@ -181,9 +199,8 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
             int32_t acc = x - run;
             for (int w = 0; w < wave; ++w) acc += s_wave[w];
             for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
+                const int32_t n = s_pref[c];
                 s_pref[c] = acc;
-                const int32_t v = p.chunk_valid[c];
-                const int32_t n = v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
                 const int64_t lo = acc > j0 ? acc : j0, hi = acc + n < j0 + tpb ? acc + n : j0 + tpb;
                 for (int64_t j = lo; j < hi; ++j) s_tok[j - j0] = c * p.chunk + (j - acc);
                 acc += n;
@@ -337,6 +354,233 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     }
 }
 
+// Pair layout, for launches without a stash and rows of 9 to 16 lane-vectors
+// (16-lane groups): each group takes one (token, operand) pair, the live pairs
+// first (in the order of the live tokens, the groups of one wavefront on one
+// operand), then runs of kPadPairs padding pairs, whose outputs are +0. A pair's
+// entries are taken in ascending batches of kFB: lane l of the group requests the
+// slot and weight of entry l mod kFB of the next batch before this batch's rows
+// and the group passes them round with DPP row broadcasts (a 16-lane group is a
+// DPP row), so each batch costs one memory round trip and the slots never pass
+// through LDS; with no staging and no stash the kernel keeps few registers, so
+// eight wavefronts per SIMD (more rows) are in flight. The same lanes, vectors
+// and fused multiply-add chain as the token-order layout: the same bits.
+constexpr int kFB = 8;
+constexpr int kPadPairs = 8;
+
+// Lane I's value of a register within each row of 16 lanes (DPP's row
+// broadcast: a VALU move, no LDS round trip); 16-, 32- or 64-bit values.
+template <int I> __device__ __forceinline__ uint32_t row_lane(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x150 + I, 0xf, 0xf, false));
+}
+template <int I, typename T> __device__ __forceinline__ T bcast(T v) {
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t x = uint64_t(v);
+        const uint64_t lo = row_lane<I>(uint32_t(x)), hi = row_lane<I>(uint32_t(x >> 32));
+        return T(lo | (hi << 32));
+    } else if constexpr (sizeof(T) == 4) {
+        uint32_t x;
+        __builtin_memcpy(&x, &v, 4);
+        x = row_lane<I>(x);
+        T r;
+        __builtin_memcpy(&r, &x, 4);
+        return r;
+    } else {
+        return T(row_lane<I>(uint32_t(v)));
+    }
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, each i a constant expression
+template <typename F, int... I> __device__ __forceinline__ void static_for_(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
+    static_for_(f, std::make_integer_sequence<int, N>{});
+}
+
+// Live pair index i -> (the pair's (token, slice) index k, operand): with two
+// operands, runs of gpw groups (one wavefront) alternate between the operands,
+// so the operand is uniform over a wavefront; indices k >= n (the live tokens
+// times the slices) name no pair (a last, partial run).
+__device__ __forceinline__ int64_t wave_pair(int64_t i, int gpw, int& op) {
+    const int64_t w = i / gpw;
+    op = int(w & 1);
+    return (w >> 1) * gpw + (i - w * gpw);
+}
+
+// One pair's entries [0, width): see the pair layout above. Entries past the
+// width repeat entry width - 1 (the same row) and feed no sum. lane_row: this
+// lane's vector of bank row 0; row_bytes: a row's bytes.
+template <typename E, int VB, typename IdxT, typename WT>
+__device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_bytes, const IdxT* idx, const WT* wts,
+                                         int width, int lane, float (&acc)[VB / sizeof(E)]) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+    using U = std::conditional_t<sizeof(IdxT) == 8, uint64_t, uint32_t>;  // slots are >= 0
+    const int e0 = lane % kFB < width ? lane % kFB : width - 1;
+    const IdxT ms0 = idx[e0];
+    WT mw = wts[e0];
+    opaque(mw);  // waited for here, with the slot, not at the loop's top
+    U sl[kFB];
+    static_for<kFB>([&](auto i) { sl[i] = U(bcast<i>(ms0)); });
+    for (int n0 = 0; n0 < width; n0 += kFB) {
+        // the next batch's slot and weight (this batch's again past the end)
+        const int nx = n0 + kFB < width ? n0 + kFB : n0;
+        const int e = nx + lane % kFB < width ? nx + lane % kFB : width - 1;
+        const IdxT ms_next = idx[e];
+        const WT mw_next = wts[e];
+        V r[kFB];
+#pragma unroll
+        for (int i = 0; i < kFB; ++i) {
+            r[i] = load_stream(reinterpret_cast<const V*>(lane_row + uint64_t(sl[i]) * row_bytes));
+            // every row load issued before any row is used, each address formed just
+            // before its load (eight addresses are not held at once)
+            asm volatile("" ::: "memory");
+        }
+        const WT wcur = mw;
+        mw = mw_next;
+        static_for<kFB>([&](auto i) {
+            const bool use = n0 + i < width;
+            const float x = value_of<WT>(bcast<i>(wcur));
+            E el[VEC];
+            __builtin_memcpy(el, &r[i], VB);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float term = __builtin_fmaf(x, widen(el[k]), acc[k]);
+                acc[k] = use ? term : acc[k];
+            }
+        });
+        static_for<kFB>([&](auto i) { sl[i] = U(bcast<i>(ms_next)); });
+    }
+}
+
+// One work unit (a live pair or a padding run) per lane group; the host sizes the
+// grid for the most units any liveness can give, and groups past the launch's
+// units exit after the block's scan of the per-chunk counts.
+template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+__global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherParams p) {
+    using V = typename RawVec<VB>::T;
+    constexpr int VEC = VB / int(sizeof(E));
+    extern __shared__ __align__(16) char s_raw[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (p.lpr - 1);
+    const int groups = kThreads / p.lpr;
+    const int slices = (p.vpr + p.lpr - 1) / p.lpr;
+
+    LiveMap m;
+    m.chunks = p.tokens / p.chunk;
+    m.chunk = p.chunk;
+    m.v = 0;
+    m.pref = nullptr;
+    if (p.chunk_valid != nullptr) {
+        // exclusive prefix of the clamped per-chunk counts (runs of chunks per
+        // thread, scanned by shuffles within a wavefront and through LDS across them)
+        int32_t* s_pref = reinterpret_cast<int32_t*>(s_raw);
+        const int64_t per = (m.chunks + kThreads - 1) / kThreads, c0 = tid * per;
+        int32_t run = 0;
+        for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
+            const int32_t v = p.chunk_valid[c];
+            const int32_t n = v < 0 ? 0 : (v > p.chunk ? int32_t(p.chunk) : v);
+            s_pref[c] = n;  // the clamped count, until this thread's pass below
+            run += n;
+        }
+        const int wl = tid & 63, wave = tid >> 6;
+        int32_t x = run;
+        for (int d = 1; d < 64; d *= 2) {
+            const int32_t y = __shfl_up(x, d);
+            x += wl >= d ? y : 0;
+        }
+        int32_t* s_wave = s_pref + m.chunks + 1;  // [kThreads / 64] wavefront totals
+        if (wl == 63) s_wave[wave] = x;
+        __syncthreads();
+        int32_t acc = x - run;
+        for (int w = 0; w < wave; ++w) acc += s_wave[w];
+        for (int64_t c = c0; c < c0 + per && c < m.chunks; ++c) {
+            const int32_t n = s_pref[c];
+            s_pref[c] = acc;
+            acc += n;
+        }
+        if (tid == kThreads - 1) s_pref[m.chunks] = acc;
+        __syncthreads();
+        m.pref = s_pref;
+    } else {
+        m.v = p.valid < p.chunk ? p.valid : p.chunk;
+    }
+    const int64_t live = m.before(m.chunks), pads = p.tokens - live;
+    const int gpw = 64 / p.lpr;
+    // live pair indices: whole pairs of runs for two operands
+    const int64_t live_ks = live * slices;
+    const int64_t live_pairs = NOPS == 2 ? (live_ks + gpw - 1) / gpw * (2 * gpw) : live_ks;
+    const int64_t pad_pairs = pads * NOPS * slices, pad_runs = (pad_pairs + kPadPairs - 1) / kPadPairs;
+    const int64_t u = int64_t(blockIdx.x) * groups + tid / p.lpr;
+    if (u >= live_pairs + pad_runs) return;
+    const E* bank = static_cast<const E*>(p.bank);
+
+    const auto store_out = [&](float* o, const float (&a)[VEC]) {
+        if (p.out_vec && VEC % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+                store_stream(reinterpret_cast<float4*>(o + e), make_float4(a[e], a[e + 1], a[e + 2], a[e + 3]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) store_stream(o + e, a[e]);
+        }
+    };
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+    if (u < live_pairs) {
+        int op = 0;
+        const int64_t k = NOPS == 2 ? wave_pair(u, gpw, op) : u;
+        if (k >= live_ks) return;
+        op = __builtin_amdgcn_readfirstlane(op);  // uniform over the wavefront (whole runs)
+        const int64_t t = m.live_at(k / slices);
+        const int vi = int(k % slices) * p.lpr + lane;
+        const int64_t col = int64_t(vi < p.vpr ? vi : p.vpr - 1) * VEC;
+        const int width = op == 0 ? p.width0 : p.width1;
+        const IdxT* idx = static_cast<const IdxT*>(op == 0 ? p.idx0 : p.idx1) + t * width;
+        const WT* wts = static_cast<const WT*>(op == 0 ? p.w0 : p.w1) + t * width;
+        const char* lane_row = reinterpret_cast<const char*>(bank + col);
+        const uint32_t row_bytes = uint32_t(p.hd * int64_t(sizeof(E)));
+        pair_sum<E, VB>(lane_row, row_bytes, idx, wts, width, lane, acc);
+        if (vi < p.vpr) store_out((op == 0 ? p.out0 : p.out1) + t * p.hd + col, acc);
+    } else {
+        // a run of padding pairs: operand-major, then token, then slice
+        const int64_t i0 = (u - live_pairs) * kPadPairs;
+        for (int64_t i = i0; i < i0 + kPadPairs && i < pad_pairs; ++i) {
+            const int op = NOPS == 2 ? int(i / (pads * slices)) : 0;
+            const int64_t k = i - op * pads * slices;
+            const int64_t t = m.pad_token(k / slices);
+            const int vi = int(k % slices) * p.lpr + lane;
+            if (vi < p.vpr) store_out((op == 0 ? p.out0 : p.out1) + t * p.hd + int64_t(vi) * VEC, acc);
+        }
+    }
+}
+
+template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+hipError_t launch_pair_typed(const GatherParams& p, hipStream_t stream) {
+    // the live pairs of every token live, rounded up to whole runs, plus gpw: the
+    // most work units a launch can hold (a padding run of kPadPairs pairs stands
+    // for fewer live pairs than it replaces, but a last run of live pairs rounded
+    // up can leave up to ceil((gpw - 1) / 4) padding runs beyond that count)
+    const int64_t groups = kThreads / p.lpr, gpw = 64 / p.lpr, ks = p.tokens * ((p.vpr + p.lpr - 1) / p.lpr);
+    const int64_t pairs = NOPS == 2 ? (ks + gpw - 1) / gpw * (2 * gpw) : ks;
+    const int64_t blocks = (pairs + gpw + groups - 1) / groups;
+    const size_t lds = p.chunk_valid ? size_t(p.tokens / p.chunk + 1 + kThreads / 64) * 4 : 0;
+    hipLaunchKernelGGL((sdm_gather_pair_kernel<E, VB, NOPS, IdxT, WT>), dim3(unsigned(blocks)), dim3(kThreads), lds,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <typename E, int VB, int NOPS>
+hipError_t launch_pair(const GatherParams& p, hipStream_t stream) {
+    if (p.idx64)
+        return p.w_bf16 ? launch_pair_typed<E, VB, NOPS, int64_t, uint16_t>(p, stream)
+                        : launch_pair_typed<E, VB, NOPS, int64_t, float>(p, stream);
+    return p.w_bf16 ? launch_pair_typed<E, VB, NOPS, int32_t, uint16_t>(p, stream)
+                    : launch_pair_typed<E, VB, NOPS, int32_t, float>(p, stream);
+}
+
 template <typename E, int VB, int NOPS, bool CMP, bool LIVE, typename IdxT, typename WT>
 hipError_t launch_typed(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
     // the live-token layout may need one more token block (its live and its padding
@@ -366,6 +610,10 @@ hipError_t launch_live(const GatherParams& p, const GatherGeometry& geo, hipStre
 // live-token layout gains nothing there).
 template <typename E, int VB, int NOPS, bool CMP>
 hipError_t launch_ops(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
+    if constexpr (!CMP) {
+        if (p.stash == nullptr && p.lpr == 16 && (p.chunk_valid == nullptr || p.tokens / p.chunk <= kLiveMaxChunks))
+            return launch_pair<E, VB, NOPS>(p, stream);
+    }
     const bool full_stash = p.stash != nullptr && !CMP;
     const bool live = !full_stash && (p.chunk_valid != nullptr ? p.tokens / p.chunk <= kLiveMaxChunks
                                                                 : p.valid < p.chunk);

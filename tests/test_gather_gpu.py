@@ -65,18 +65,24 @@ CASES = [
     ("hd600 bf16 two slices", torch.bfloat16, 500, 600, 16, 8, 9, 4, torch.int32, torch.float32),
     ("hd1000 f32 four slices", torch.float32, 200, 1000, 8, 4, 5, 3, torch.int64, torch.float32),
     ("hd128 bf16 widths 255/97", torch.bfloat16, 4000, 128, 40, 8, 255, 97, torch.int32, torch.bfloat16),
+    # rows of 9 to 16 vectors (16-lane groups) with lanes past the row, narrow widths
+    ("hd120 bf16 15 vectors", torch.bfloat16, 3000, 120, 96, 16, 40, 23, torch.int32, torch.bfloat16),
+    ("hd40 f32 10 vectors", torch.float32, 2000, 40, 64, 8, 9, 16, torch.int64, torch.float32),
+    ("hd9 bf16 2-B vectors", torch.bfloat16, 500, 9, 64, 16, 7, 8, torch.int32, torch.float32),
+    ("hd128 bf16 widths 3/1", torch.bfloat16, 2000, 128, 70, 7, 3, 1, torch.int64, torch.bfloat16),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("padding", ["per_chunk", "scalar", "none", "all"])
-def test_small_cases(case, padding):
+@pytest.mark.parametrize("stash", [True, False], ids=["stash", "no-stash"])
+def test_small_cases(case, padding, stash):
     name, dt, slots, hd, T, chunk, W0, W1, idt, wdt = case
     wl = gen.GatherWorkload(name=name, bank_dtype=dt, num_slots=slots, head_dim=hd, tokens=T, chunk=chunk,
                             valid_low=0, valid_high=chunk, width0=W0, width1=W1, idx_dtype=idt, w_dtype=wdt,
                             bank_std=0.5)
     valid = {"per_chunk": None, "scalar": max(1, chunk // 2), "none": chunk, "all": 0}[padding]
-    run_case(wl, 11, per_chunk=padding == "per_chunk", valid=valid)
+    run_case(wl, 11, per_chunk=padding == "per_chunk", valid=valid, stash=stash)
 
 
 @pytest.mark.parametrize("stash", [True, False])
@@ -116,25 +122,30 @@ def test_errors_from_python():
 
 def check_c3(wl, bank, inp, out0, stash, out1):
     """c3's outputs: sampled tokens against the oracle bit for bit; every padding token
-    zero and every live stash row equal to its bank row."""
+    zero and every live stash row equal to its bank row (stash None: no stash; out1
+    None: operand 0 only)."""
     T = wl.tokens
+    two = out1 is not None
     t = torch.arange(T, device=DEV)
     live = (t % wl.chunk) < inp["chunk_valid"].long()[t // wl.chunk]
     _say(f"  live tokens {int(live.sum())} of {T}")
     # padding: zero bits everywhere
-    assert not out0[~live].view(torch.int32).any() and not out1[~live].view(torch.int32).any()
-    assert not stash[~live].view(torch.int16).any()
-    # stash: raw rows of operand 0 for every live token (checked in slices)
-    lt = t[live]
-    for i in range(0, lt.numel(), 2048):
-        sel = lt[i:i + 2048]
-        rows = bank[inp["idx0"][sel].long()]
-        assert torch.equal(stash[sel].view(torch.int16), rows.view(torch.int16))
+    assert not out0[~live].view(torch.int32).any()
+    if two:
+        assert not out1[~live].view(torch.int32).any()
+    if stash is not None:
+        assert not stash[~live].view(torch.int16).any()
+        # stash: raw rows of operand 0 for every live token (checked in slices)
+        lt = t[live]
+        for i in range(0, lt.numel(), 2048):
+            sel = lt[i:i + 2048]
+            rows = bank[inp["idx0"][sel].long()]
+            assert torch.equal(stash[sel].view(torch.int16), rows.view(torch.int16))
     # sampled tokens against the oracle (bank rows they touch, renumbered)
     g = torch.Generator().manual_seed(1)
     sample = torch.cat([torch.randperm(T, generator=g)[:1024], torch.arange(0, 128)]).unique().to(DEV)
     idx0 = inp["idx0"][sample].long()
-    idx1 = inp["idx1"][sample].long()
+    idx1 = inp["idx1"][sample].long() if two else idx0[:, :0]
     uniq, inv = torch.unique(torch.cat([idx0.ravel(), idx1.ravel()]), return_inverse=True)
     sub_bank = to_np_bank(bank[uniq])
     n0 = idx0.numel()
@@ -143,10 +154,13 @@ def check_c3(wl, bank, inp, out0, stash, out1):
     live_s = live[sample].cpu().numpy().astype(np.int32)
     # one-token chunks whose valid count is the token's liveness reproduce the padding rule
     ref0, ref_st, ref1 = oracle.gather(sub_bank, i0, _np(inp["w0"][sample]), chunk=1, chunk_valid=live_s,
-                                       idx1=i1, w1=_np(inp["w1"][sample]))
+                                       idx1=i1 if two else None, w1=_np(inp["w1"][sample]) if two else None,
+                                       stash=stash is not None)
     assert bits_equal(_np(out0[sample]), ref0)
-    assert bits_equal(_np(out1[sample]), ref1)
-    assert bits_equal(to_np_bank(stash[sample]), ref_st)
+    if two:
+        assert bits_equal(_np(out1[sample]), ref1)
+    if stash is not None:
+        assert bits_equal(to_np_bank(stash[sample]), ref_st)
 
 
 @pytest.mark.slow
@@ -161,6 +175,24 @@ def test_full_size_c3():
     torch.cuda.synchronize()
     check_c3(wl, bank, inp, out0, stash, out1)
     del bank, stash
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("two", [True, False], ids=["two-ops", "one-op"])
+def test_full_size_c3_without_stash(two):
+    """Config c3's tokens at full size with no stash, both operands or operand 0
+    only, one eager launch (the launch shapes that take the pair layout)."""
+    wl = gen.WORKLOADS["c3"]
+    bank = gen.gather_bank(wl, 0, DEV)
+    inp = gen.gather_inputs(wl, 0, DEV)
+    kw = dict(idx1=inp["idx1"], w1=inp["w1"]) if two else {}
+    out0, stash, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, chunk_valid=inp["chunk_valid"],
+                                   with_stash=False, **kw)
+    torch.cuda.synchronize()
+    assert stash is None and (out1 is not None) == two
+    check_c3(wl, bank, inp, out0, None, out1)
+    del bank
     torch.cuda.empty_cache()
 
 
@@ -192,7 +224,8 @@ def test_full_size_c3_graph_replays():
     torch.cuda.empty_cache()
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("with_stash", [True, False], ids=["stash", "no-stash"])
+def test_graph_replays_match_eager(with_stash):
     """The benchmark's launch path: sdm_gather captured in a HIP graph. Every replay, with
     eager torch work and synchronisations between replays and the outputs cleared
     first, must equal an eager launch bit for bit."""
@@ -200,22 +233,25 @@ def test_graph_replays_match_eager():
     bank = gen.gather_bank(wl, 21, DEV)
     inp = gen.gather_inputs(wl, 21, DEV)
     kw = dict(chunk=wl.chunk, chunk_valid=inp["chunk_valid"], idx1=inp["idx1"], w1=inp["w1"])
-    r0, rs, r1 = sdm_gather(bank, inp["idx0"], inp["w0"], **kw)
-    out0, stash, out1 = torch.empty_like(r0), torch.empty_like(rs), torch.empty_like(r1)
+    r0, rs, r1 = sdm_gather(bank, inp["idx0"], inp["w0"], **kw, with_stash=with_stash)
+    out0, out1 = torch.empty_like(r0), torch.empty_like(r1)
+    stash = torch.empty_like(rs) if with_stash else None
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        sdm_gather(bank, inp["idx0"], inp["w0"], **kw, out0=out0, out1=out1, stash=stash)
+        sdm_gather(bank, inp["idx0"], inp["w0"], **kw, out0=out0, out1=out1, stash=stash, with_stash=with_stash)
     for i in range(3):
         out0.fill_(7.0)
         out1.fill_(7.0)
-        stash.fill_(7.0)
+        if with_stash:
+            stash.fill_(7.0)
         junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out0.view(torch.int32), r0.view(torch.int32)), f"replay {i}"
         assert torch.equal(out1.view(torch.int32), r1.view(torch.int32)), f"replay {i}"
-        assert torch.equal(stash.view(torch.int16), rs.view(torch.int16)), f"replay {i}"
+        if with_stash:
+            assert torch.equal(stash.view(torch.int16), rs.view(torch.int16)), f"replay {i}"
         del junk
 
 
@@ -270,7 +306,8 @@ print(call2([[1], [2], [9], [-5]], [1, 2]))
 
 @pytest.mark.parametrize("per_chunk", [True, False])
 @pytest.mark.parametrize("idt", [torch.int32, torch.int64])
-def test_padding_slots_are_never_read(per_chunk, idt):
+@pytest.mark.parametrize("with_stash", [True, False], ids=["stash", "no-stash"])
+def test_padding_slots_are_never_read(per_chunk, idt, with_stash):
     """Slots of padding tokens set to -1 or far past the bank: the kernel reads no row
     for them (padding outputs are zeros, stash rows zero), so every result equals
     the oracle's on the same arrays, bit for bit."""
@@ -289,11 +326,13 @@ def test_padding_slots_are_never_read(per_chunk, idt):
         inp[name][pad] = junk
     cv = inp["chunk_valid"] if per_chunk else None
     out0, st, out1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=wl.chunk, valid=valid, chunk_valid=cv,
-                                idx1=inp["idx1"], w1=inp["w1"])
+                                idx1=inp["idx1"], w1=inp["w1"], with_stash=with_stash)
     torch.cuda.synchronize()
     ref0, ref_st, ref1 = oracle.gather(
         to_np_bank(bank), _np(inp["idx0"]), _np(inp["w0"]), chunk=wl.chunk, valid=valid,
-        chunk_valid=None if cv is None else _np(cv), idx1=_np(inp["idx1"]), w1=_np(inp["w1"]))
+        chunk_valid=None if cv is None else _np(cv), idx1=_np(inp["idx1"]), w1=_np(inp["w1"]), stash=with_stash)
     assert bits_equal(_np(out0), ref0) and bits_equal(_np(out1), ref1)
-    assert bits_equal(to_np_bank(st), ref_st)
-    assert not _np(out0)[pad.cpu().numpy()].any() and not to_np_bank(st)[pad.cpu().numpy()].any()
+    assert not _np(out0)[pad.cpu().numpy()].any()
+    if with_stash:
+        assert bits_equal(to_np_bank(st), ref_st)
+        assert not to_np_bank(st)[pad.cpu().numpy()].any()

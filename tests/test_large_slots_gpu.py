@@ -79,7 +79,19 @@ def test_decode_slots_past_2_31(big_bank):
 
 
 def test_gather_slots_past_2_31(big_bank):
-    bank = big_bank
+    gather_past_2_31(big_bank, with_stash=True)
+
+
+def test_gather_pair_layout_slots_past_2_31():
+    """Rows of nine bfloat16 elements (nine 2-byte vectors, one 16-lane group per
+    pair) and no stash: the launch shape of the pair layout."""
+    bank = torch.zeros((ROWS, 9), dtype=torch.bfloat16, device=DEV)
+    gather_past_2_31(bank, with_stash=False)
+    del bank
+    torch.cuda.empty_cache()
+
+
+def gather_past_2_31(bank, with_stash):
     hd = bank.shape[1]
     rng = np.random.default_rng(32)
     lo = (1 << 31) - 1024  # slots drawn from [lo, ROWS): a fifth below row 2^31
@@ -93,13 +105,17 @@ def test_gather_slots_past_2_31(big_bank):
     w1 = _bf16_bits(rng, (T, W1), 1.0)
     wf0 = (w0.astype(np.uint32) << 16).view(np.float32)
     wf1 = (w1.astype(np.uint32) << 16).view(np.float32)
-    ref0, ref_st, ref1 = oracle.gather(init, idx0 - lo, wf0, chunk=chunk, chunk_valid=cv, idx1=idx1 - lo, w1=wf1)
+    ref0, ref_st, ref1 = oracle.gather(init, idx0 - lo, wf0, chunk=chunk, chunk_valid=cv, idx1=idx1 - lo, w1=wf1,
+                                       stash=with_stash)
 
     def dev(a):
         return torch.from_numpy(a).to(DEV)
 
     out0, stash, out1 = sdm_gather(bank, dev(idx0), from_np_bank(w0).to(DEV), chunk=chunk, chunk_valid=dev(cv),
-                                   idx1=dev(idx1), w1=from_np_bank(w1).to(DEV))
+                                   idx1=dev(idx1), w1=from_np_bank(w1).to(DEV), with_stash=with_stash)
     assert bits_equal(out0.cpu().numpy(), ref0), "operand 0 differs from the oracle"
     assert bits_equal(out1.cpu().numpy(), ref1), "operand 1 differs from the oracle"
-    assert bits_equal(to_np_bank(stash), ref_st), "stash differs from the oracle"
+    if with_stash:
+        assert bits_equal(to_np_bank(stash), ref_st), "stash differs from the oracle"
+    else:
+        assert stash is None
