@@ -76,8 +76,13 @@ def kernel_pattern(kind: str) -> str:
 
 
 # Name fragment that selects a launch kind's kernels in a rocprofv3 trace (the
-# multi-token decode has two loops; the library picks one per launch shape).
-KERNEL_PATTERN = {"gather": "sdm_gather_kernel", "steps": "sdm_decode_steps", "step": "sdm_decode_kernel"}
+# multi-token decode has two loops and the gather two layouts; the library picks
+# one per launch shape).
+KERNEL_PATTERN = {"gather": "sdm_gather_", "steps": "sdm_decode_steps", "step": "sdm_decode_kernel"}
+
+# Gather launch shapes: (both operands, stash), as bench.py --gather names them.
+GATHER_SHAPES = {"two-ops": (True, True), "one-op": (False, True), "no-stash": (True, False),
+                 "one-op-no-stash": (False, False)}
 
 
 def stored_traffic(config: str, kind: str, tokens_per_launch: int = 1, live_tokens=None):
@@ -818,12 +823,13 @@ def derived_counters(c: dict) -> dict:
     return out
 
 
-def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0) -> tuple:
+def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0, gather: str = "two-ops") -> tuple:
     """(bytes per launch, unit description, launch shape) of the row traffic the method
-    needs, for the launch the benchmark runs with these arguments. The shape holds the
-    launch's tokens per stream (decode) or its live-token count (gather); the live
-    count comes from the same draw the benchmark launches (gen draws the per-chunk
-    counts on the CPU for every device)."""
+    needs, for the launch the benchmark runs with these arguments (gather: the launch
+    shape, one of GATHER_SHAPES). The shape holds the launch's tokens per stream
+    (decode) or its live-token count (gather); the live count comes from the same
+    draw the benchmark launches (gen draws the per-chunk counts on the CPU for every
+    device)."""
     import gen
     import torch
     wl = gen.WORKLOADS[cfg_name]
@@ -834,17 +840,21 @@ def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0) -> tuple:
         return (per * tokens,
                 f"{tokens} token(s) x {wl.streams} streams x (2W+R)={2 * wl.W + wl.R} rows x {wl.head_dim * es} B",
                 {"tokens_per_launch": tokens})
+    two, with_stash = GATHER_SHAPES[gather]
     live = gen.live_tokens(wl, gen.gather_inputs(wl.replace(width0=1, width1=0), seed)["chunk_valid"])
-    rows = live * (wl.width0 + wl.width1) * wl.head_dim * es + wl.tokens * wl.width0 * wl.head_dim * es
-    return (rows, f"{live} live tokens x {wl.width0 + wl.width1} rows read + {wl.tokens} x {wl.width0} stash rows, "
-                  f"x {wl.head_dim * es} B", {"tokens_per_launch": wl.tokens, "live_tokens": live})
+    read = wl.width0 + (wl.width1 if two else 0)
+    stash_rows = wl.tokens * wl.width0 if with_stash else 0
+    rows = (live * read + stash_rows) * wl.head_dim * es
+    return (rows, f"{live} live tokens x {read} rows read + {stash_rows} stash rows, x {wl.head_dim * es} B",
+            {"tokens_per_launch": wl.tokens, "live_tokens": live})
 
 
 def ingest_profile(args) -> int:
     trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
-    if args.config == "c3" and args.gather != "two-ops":
-        raise SystemExit("bench.py: profiles are summarised for the workload's own launch shape only")
-    kind = launch_kind(args.config, args.entry)
+    if args.config == "c3" and (args.gather not in GATHER_SHAPES or args.valid != "per-chunk" or args.tokens):
+        raise SystemExit("bench.py: gather profiles are summarised for c3's own tokens and per-chunk counts, "
+                         f"in the launch shapes {sorted(GATHER_SHAPES)}")
+    kind = launch_kind(args.config, args.entry, args.gather)
     pattern = kernel_pattern(kind)
     stats = [r for r in _csv_rows(trace, "kernel_stats.csv") if pattern in r["Name"]]
     if not stats:
@@ -862,7 +872,7 @@ def ingest_profile(args) -> int:
     cw_kib, _ = _counter_kib(copy_write, "elementwise", min_kib=gib_kib / 8)
     f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
     fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
-    alg, alg_desc, shape = algorithmic_bytes(args.config, args.entry, args.seed)
+    alg, alg_desc, shape = algorithmic_bytes(args.config, args.entry, args.seed, args.gather)
     raw = {}
     for d in args.extra_counters:
         raw.update(_counters(d, kernel))
@@ -880,9 +890,11 @@ def ingest_profile(args) -> int:
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
-    md = os.path.join(PROFILES, f"{kernel}_{args.config}.md")
+    shape_tag = "" if kind in ("gather", "steps", "step") else "_" + kind[len("gather-"):]
+    md = os.path.join(PROFILES, f"{kernel}_{args.config}{shape_tag}.md")
     with open(md, "w") as f:
-        f.write(f"# {kernel} on workload {args.config} (MI355X, rocprofv3)\n\n")
+        f.write(f"# {kernel} on workload {args.config}{' [' + shape_tag[1:] + ']' if shape_tag else ''} "
+                "(MI355X, rocprofv3)\n\n")
         f.write(f"Kernel sources hash {kernel_source_hash()} (bench.py `kernel_source_hash`).\n\n")
         f.write("## Commands\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")
         f.write("## Kernel trace (`--kernel-trace --stats`)\n\n| kernel | calls | average | min | max |\n|---|---|---|---|---|\n")

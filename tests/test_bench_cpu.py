@@ -50,8 +50,9 @@ def test_launch_kinds():
     # the gather's other launch shapes never pick up the workload's stored traffic
     assert bench.launch_kind("c3", "steps", "one-op") == "gather-one-op"
     assert bench.launch_kind("c3", "steps", "compact") == "gather-compact"
-    assert bench.kernel_pattern("gather-no-stash") == "sdm_gather_kernel"
-    assert bench.kernel_pattern("gather-compact") == "sdm_gather_kernel"
+    assert bench.kernel_pattern("gather-no-stash") == "sdm_gather_"
+    assert "sdm_gather_" in "sdm_gather_kernel" and "sdm_gather_" in "sdm_gather_pair_kernel"
+    assert bench.kernel_pattern("gather-compact") == "sdm_gather_"
 
 
 def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
@@ -123,6 +124,44 @@ def test_gather_traffic_needs_the_same_live_tokens(tmp_path, monkeypatch):
     assert bench.stored_traffic("c3", "gather", 32768, shape["live_tokens"])[0] == pytest.approx(
         (700000.0 * 2 + 600000.0) * 1024)
     assert bench.stored_traffic("c3", "gather", 32768, shape["live_tokens"] - 1) == (None, None)
+
+
+def test_gather_shapes_profile_under_their_own_kind(tmp_path, monkeypatch):
+    """A launch shape without a stash runs the pair layout: its profile is stored under
+    its own kind, with the shape's algorithmic bytes, in a summary named for the shape."""
+    import gen
+    import torch
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    g = "void sdm::(anonymous namespace)::sdm_gather_pair_kernel<unsigned short, 16, 2, int, unsigned short>(sdm::GatherParams)"
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    _trace(t, [(g, 10, 150000.0)])
+    _counter(f, [(g, 300000.0)])
+    _counter(w, [(g, 20000.0)])
+    _counter(cf, [(COPY, 524288.0)])
+    _counter(cw, [(COPY, 1048576.0)])
+    assert bench.main(["--config", "c3", "--gather", "no-stash", "--ingest-profile", t, f, w, cf, cw]) == 0
+    with open(tmp_path / "profiles" / "traffic.json") as fh:
+        data = json.load(fh)
+    assert set(data) == {"c3/gather-no-stash"}
+    e = data["c3/gather-no-stash"]
+    assert e["kernel"] == "sdm_gather_pair_kernel"
+    wl = gen.WORKLOADS["c3"]
+    row = wl.head_dim * torch.empty((), dtype=wl.bank_dtype).element_size()
+    live = e["live_tokens"]
+    assert e["algorithmic_bytes_per_launch"] == live * (wl.width0 + wl.width1) * row
+    assert (tmp_path / "profiles" / "sdm_gather_pair_kernel_c3_no-stash.md").exists()
+    assert bench.stored_traffic("c3", "gather-no-stash", wl.tokens, live)[1] == "sdm_gather_pair_kernel"
+    assert bench.stored_traffic("c3", "gather", wl.tokens, live) == (None, None)
+    # the other shapes' bytes
+    assert bench.algorithmic_bytes("c3", "steps", 0, "one-op-no-stash")[0] == live * wl.width0 * row
+    assert bench.algorithmic_bytes("c3", "steps", 0, "one-op")[0] == (live + wl.tokens) * wl.width0 * row
+    assert bench.algorithmic_bytes("c3", "steps", 0, "two-ops")[0] == (
+        live * (wl.width0 + wl.width1) + wl.tokens * wl.width0) * row
+    # compact stashes and other paddings are not summarised
+    with pytest.raises(SystemExit):
+        bench.main(["--config", "c3", "--gather", "compact", "--ingest-profile", t, f, w, cf, cw])
+    with pytest.raises(SystemExit):
+        bench.main(["--config", "c3", "--gather", "no-stash", "--valid", "all", "--ingest-profile", t, f, w, cf, cw])
 
 
 def test_gather_live_count_does_not_depend_on_the_device():
