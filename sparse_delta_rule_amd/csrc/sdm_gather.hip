@@ -50,36 +50,57 @@ constexpr int kLiveMaxChunks = 4096; // most chunks a launch in the live-token l
 // N consecutive entries [n0, n0 + N) of one operand, all valid: every row load
 // is issued before the first row is used, and each row feeds the sum
 // unconditionally (a row used only under a branch would have its load moved
-// next to that use and waited for there). stash_row: this token's stash rows,
-// or (CMP) its chunk's block of crow rows, whose row s_kp[k] an entry names (a
-// position outside [0, crow) stores nothing); NULL for none.
+// next to that use and waited for there). Registers: each row address is formed
+// just before its load, the sums are taken as the rows arrive with the weights
+// read four at a time, and only then are the stash rows stored under one branch
+// (stores under a branch per row made the compiler hold every address and every
+// weight across the batch). stash_row: this token's stash rows, or (CMP) its
+// chunk's block of crow rows, whose row s_kp[k] an entry names (a position
+// outside [0, crow) stores nothing); NULL for none.
 template <typename E, int VB, int N, bool CMP, typename IdxT, typename WT>
 __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t hd, int64_t col, int n0, int k0,
                                              const IdxT* s_idx, const WT* s_w, const int32_t* s_kp, E* stash_row,
                                              int64_t crow, float (&acc)[VB / sizeof(E)]) {
     using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
+    using U = std::conditional_t<sizeof(IdxT) == 8, uint64_t, uint32_t>;  // slots are >= 0
+    const char* lane_row = reinterpret_cast<const char*>(bank + col);
+    const uint32_t row_bytes = uint32_t(hd * int64_t(sizeof(E)));
     V r[N];
-    float x[N];
+    // four slots read from LDS at a time, each row's address formed just before its
+    // load (a compiler barrier after each load: N addresses are never held at once)
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        r[i] = load_stream(reinterpret_cast<const V*>(bank + int64_t(s_idx[k0 + i]) * hd + col));
-        x[i] = value_of<WT>(s_w[k0 + i]);
-    }
+    for (int i0 = 0; i0 < N; i0 += 4) {
+        U sl[4];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        if constexpr (CMP) {
-            if (stash_row != nullptr) {
-                const int32_t kp = s_kp[k0 + i];
-                if (kp >= 0 && kp < crow) store_stream(reinterpret_cast<V*>(stash_row + int64_t(kp) * hd + col), r[i]);
-            }
-        } else if (stash_row != nullptr) {
-            store_stream(reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col), r[i]);
+        for (int j = 0; j < 4 && i0 + j < N; ++j) sl[j] = U(s_idx[k0 + i0 + j]);
+#pragma unroll
+        for (int j = 0; j < 4 && i0 + j < N; ++j) {
+            r[i0 + j] = load_stream(reinterpret_cast<const V*>(lane_row + uint64_t(sl[j]) * row_bytes));
+            asm volatile("" ::: "memory");
         }
+    }
+    // the sums first, as the rows arrive (weights read from LDS four at a time, not
+    // all N ahead), then the stash stores under one branch
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (i % 4 == 0) asm volatile("" ::: "memory");
+        const float x = value_of<WT>(s_w[k0 + i]);
         E el[VEC];
         __builtin_memcpy(el, &r[i], VB);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(x[i], widen(el[e]), acc[e]);
+        for (int e = 0; e < VEC; ++e) acc[e] = __builtin_fmaf(x, widen(el[e]), acc[e]);
+    }
+    if (stash_row != nullptr) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if constexpr (CMP) {
+                const int32_t kp = s_kp[k0 + i];
+                if (kp >= 0 && kp < crow) store_stream(reinterpret_cast<V*>(stash_row + int64_t(kp) * hd + col), r[i]);
+            } else {
+                store_stream(reinterpret_cast<V*>(stash_row + int64_t(n0 + i) * hd + col), r[i]);
+            }
+        }
     }
 }
 
