@@ -49,11 +49,22 @@ PROFILES = os.path.join(ROOT, "profiles")
 STORAGE_DTYPE = {"torch.bfloat16": "bf16", "torch.float32": "f32"}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP kernel sources' code (comments and whitespace removed); stored
-    HBM-traffic figures are valid only for it."""
+# The sources a launch kind's kernels are built from (besides the shared header
+# and the C ABI, which sets up every launch).
+KIND_SOURCES = {"decode": "sdm_decode.hip", "gather": "sdm_gather.hip"}
+
+
+def kernel_source_hash(kind: str = None) -> str:
+    """Hash of the HIP kernel sources' code (comments and whitespace removed): of the
+    shared header, the C ABI and the kind's own kernel file (a decode kind: "step",
+    "steps"; a gather kind: "gather..."), or of every source (kind None). Stored
+    HBM-traffic figures are valid only for the hash of their kind."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "sparse_delta_rule_amd", "csrc", "*"))):
+    paths = sorted(glob.glob(os.path.join(ROOT, "sparse_delta_rule_amd", "csrc", "*")))
+    if kind is not None:
+        own = KIND_SOURCES["gather" if kind.startswith("gather") else "decode"]
+        paths = [p for p in paths if os.path.basename(p) in (own, "sdm_kernels.h", "sdm_api.hip")]
+    for p in paths:
         with open(p, encoding="utf-8") as f:
             text = f.read()
         code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -101,7 +112,7 @@ def stored_traffic(config: str, kind: str, tokens_per_launch: int = 1, live_toke
     with open(path) as f:
         data = json.load(f)
     entry = data.get(f"{config}/{kind}")
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(kind):
         return None, None
     stored_tokens = entry.get("tokens_per_launch")
     if not stored_tokens or not entry.get("bytes_per_launch"):
@@ -883,7 +894,7 @@ def ingest_profile(args) -> int:
         with open(traffic_path) as f:
             data = json.load(f)
     data[f"{args.config}/{kind}"] = {
-        "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fetch_b + write_b,
+        "kernel_source_hash": kernel_source_hash(kind), "bytes_per_launch": fetch_b + write_b,
         "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
         "algorithmic_bytes_per_launch": alg, "avg_kernel_ns": avg_ns, "calls": calls, "kernel": kernel,
         "counters": raw, **shape, **derived}
@@ -895,7 +906,8 @@ def ingest_profile(args) -> int:
     with open(md, "w") as f:
         f.write(f"# {kernel} on workload {args.config}{' [' + shape_tag[1:] + ']' if shape_tag else ''} "
                 "(MI355X, rocprofv3)\n\n")
-        f.write(f"Kernel sources hash {kernel_source_hash()} (bench.py `kernel_source_hash`).\n\n")
+        f.write(f"Kernel sources hash {kernel_source_hash(kind)} (bench.py `kernel_source_hash` of launch kind "
+                f"`{kind}`).\n\n")
         f.write("## Commands\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")
         f.write("## Kernel trace (`--kernel-trace --stats`)\n\n| kernel | calls | average | min | max |\n|---|---|---|---|---|\n")
         for r in stats:
@@ -987,7 +999,8 @@ def ingest_stream_sweep(args) -> int:
     os.makedirs(PROFILES, exist_ok=True)
     with open(md, "w") as f:
         f.write(f"# {pattern} on workload {args.config} over stream counts (MI355X, rocprofv3 kernel trace)\n\n")
-        f.write(f"Kernel sources hash {kernel_source_hash()} (bench.py `kernel_source_hash`). Each stream keeps "
+        f.write(f"Kernel sources hash {kernel_source_hash(kind)} (bench.py `kernel_source_hash` of launch kind "
+                f"`{kind}`). Each stream keeps "
                 f"its {wl.slots_per_stream} slots, so the bank grows with the stream count; {tokens} token(s) per "
                 f"launch, {per_stream} algorithmic row bytes per stream per launch.\n\n")
         f.write("## Command\n\n```\n" + args.profile_commands.strip() + "\n```\n\n")

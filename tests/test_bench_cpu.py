@@ -84,7 +84,7 @@ def test_ingest_scales_counters_and_keys_by_launch_kind(tmp_path, monkeypatch):
     # a multi-token figure never stands for a single-token launch (another kernel)
     assert bench.stored_traffic("c1", "steps", 1) == (None, None)
     assert bench.stored_traffic("c1", "step", 1) == (None, None)
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kind=None: "0" * 16)
     assert bench.stored_traffic("c1", "steps", 64) == (None, None)
 
 
@@ -227,6 +227,30 @@ def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     (src / "k.hip").write_text("int f(int x) { return x + 2; }\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_kernel_hash_of_a_kind_covers_its_own_sources(tmp_path, monkeypatch):
+    """A gather-only change leaves the decode kinds' stored figures valid, and the
+    reverse; the shared header and the C ABI count for both."""
+    src = tmp_path / "sparse_delta_rule_amd" / "csrc"
+    src.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for n in ("sdm_decode.hip", "sdm_gather.hip", "sdm_kernels.h", "sdm_api.hip", "sdm_convert.hip"):
+        (src / n).write_text(f"int {n.split('.')[0]}() {{ return 0; }}\n")
+    h = {k: bench.kernel_source_hash(k) for k in ("step", "steps", "gather", "gather-no-stash")}
+    assert h["step"] == h["steps"] and h["gather"] == h["gather-no-stash"] and h["step"] != h["gather"]
+
+    def changed(name, text):
+        (src / name).write_text(text)
+        return {k: bench.kernel_source_hash(k) != v for k, v in h.items()}
+    assert changed("sdm_gather.hip", "int g() { return 1; }\n") == {
+        "step": False, "steps": False, "gather": True, "gather-no-stash": True}
+    (src / "sdm_gather.hip").write_text("int sdm_gather() { return 0; }\n")
+    assert changed("sdm_decode.hip", "int d() { return 1; }\n") == {
+        "step": True, "steps": True, "gather": False, "gather-no-stash": False}
+    (src / "sdm_decode.hip").write_text("int sdm_decode() { return 0; }\n")
+    assert not any(changed("sdm_convert.hip", "int c() { return 1; }\n").values())
+    assert all(changed("sdm_kernels.h", "int k() { return 1; }\n").values())
 
 
 # ------------------------------------------------------------ CPU baseline legs
