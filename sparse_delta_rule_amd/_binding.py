@@ -223,7 +223,7 @@ def _gather_operands(bank, idx0, w0, chunk, valid, chunk_valid, idx1, w1, out0, 
     dev = bank.device
     two = idx1 is not None
     if two != (w1 is not None):
-        raise ValueError("idx1 and w1 go together")
+        raise ValueError("give both idx1 and w1 for a second operand, or neither")
     W1 = 0
     if two:
         if idx1.dim() != 2 or tuple(w1.shape) != tuple(idx1.shape) or idx1.shape[0] != tokens:
@@ -347,7 +347,7 @@ def sdm_gather_plan(bank: torch.Tensor, idx0: torch.Tensor, w0: torch.Tensor, *,
     dev = bank.device
     two = idx1 is not None
     if two != (w1 is not None):
-        raise ValueError("idx1 and w1 go together")
+        raise ValueError("give both idx1 and w1 for a second operand, or neither")
     W1 = 0
     if two:
         if idx1.dim() != 2 or tuple(w1.shape) != tuple(idx1.shape) or idx1.shape[0] != rows:

@@ -416,3 +416,17 @@ def test_binding_rejects_decode_dtypes_and_readings():
     # on the CPU the shapes pass and the device check refuses
     with pytest.raises(ValueError, match="is on cpu"):
         sdm.sdm_decode_steps(torch.zeros(64, 8), **_decode_tensors(steps=2))
+
+
+@pytest.mark.parametrize("give", ["idx1", "w1"])
+def test_binding_wants_both_arrays_of_a_second_operand(give):
+    import torch
+    from sparse_delta_rule_amd import sdm_gather, sdm_gather_compact
+    bank = torch.zeros(10, 4)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    w = torch.zeros(4, 2)
+    extra = {give: idx if give == "idx1" else w}
+    with pytest.raises(ValueError, match="give both idx1 and w1"):
+        sdm_gather(bank, idx, w, chunk=4, **extra)
+    with pytest.raises(ValueError, match="give both idx1 and w1"):
+        sdm_gather_compact(bank, idx, w, torch.zeros(4, 2, dtype=torch.int32), chunk=4, **extra)
