@@ -69,6 +69,9 @@ CASES = [
     ("hd120 bf16 15 vectors", torch.bfloat16, 3000, 120, 96, 16, 40, 23, torch.int32, torch.bfloat16),
     ("hd40 f32 10 vectors", torch.float32, 2000, 40, 64, 8, 9, 16, torch.int64, torch.float32),
     ("hd9 bf16 2-B vectors", torch.bfloat16, 500, 9, 64, 16, 7, 8, torch.int32, torch.float32),
+    ("hd30 bf16 4-B vectors", torch.bfloat16, 700, 30, 48, 12, 11, 5, torch.int64, torch.bfloat16),
+    ("hd36 bf16 8-B vectors", torch.bfloat16, 900, 36, 80, 20, 16, 24, torch.int32, torch.bfloat16),
+    ("hd18 f32 8-B vectors", torch.float32, 600, 18, 36, 9, 8, 0, torch.int32, torch.float32),
     ("hd128 bf16 widths 3/1", torch.bfloat16, 2000, 128, 70, 7, 3, 1, torch.int64, torch.bfloat16),
 ]
 
@@ -105,6 +108,28 @@ def test_misaligned_views_take_narrow_vectors():
                                        chunk_valid=_np(inp["chunk_valid"][:4]), idx1=_np(inp["idx1"]),
                                        w1=_np(inp["w1"]))
     assert bits_equal(_np(o0), ref0) and bits_equal(_np(o1), ref1) and bits_equal(to_np_bank(st), ref_st)
+
+
+@pytest.mark.parametrize("with_stash", [True, False], ids=["stash", "no-stash"])
+def test_misaligned_outputs_take_element_stores(with_stash):
+    """Outputs one float past 16-byte alignment on an aligned bank (the pair layout
+    without a stash): the outputs are stored element by element, the bits unchanged."""
+    wl = gen.WORKLOADS["c3"].replace(num_slots=4000, tokens=128, chunk=16, valid_low=3, valid_high=16)
+    bank = gen.gather_bank(wl, 14).to(DEV)
+    inp = {k: v.to(DEV) for k, v in gen.gather_inputs(wl, 14).items()}
+    buf0 = torch.full((128 * 128 + 1,), float("nan"), device=DEV)
+    buf1 = torch.full((128 * 128 + 1,), float("nan"), device=DEV)
+    out0, out1 = buf0[1:].view(128, 128), buf1[1:].view(128, 128)
+    o0, st, o1 = sdm_gather(bank, inp["idx0"], inp["w0"], chunk=16, chunk_valid=inp["chunk_valid"],
+                            idx1=inp["idx1"], w1=inp["w1"], out0=out0, out1=out1, with_stash=with_stash)
+    torch.cuda.synchronize()
+    ref0, ref_st, ref1 = oracle.gather(to_np_bank(bank), _np(inp["idx0"]), _np(inp["w0"]), chunk=16,
+                                       chunk_valid=_np(inp["chunk_valid"]), idx1=_np(inp["idx1"]),
+                                       w1=_np(inp["w1"]), stash=with_stash)
+    assert bits_equal(_np(o0), ref0) and bits_equal(_np(o1), ref1)
+    assert torch.isnan(buf0[0]) and torch.isnan(buf1[0])  # nothing written before the views
+    if with_stash:
+        assert bits_equal(to_np_bank(st), ref_st)
 
 
 def test_errors_from_python():
