@@ -1,0 +1,136 @@
+"""The gather kernels' index arithmetic, restated and checked on the CPU: every
+mapping from a workgroup or lane group to its work is a bijection onto the work,
+and the pair layout's grid holds every unit any liveness can give. Each function
+below restates one formula of sparse_delta_rule_amd/csrc/sdm_gather.hip (named in
+its docstring); the constants are read from that source."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = open(os.path.join(ROOT, "sparse_delta_rule_amd", "csrc", "sdm_gather.hip")).read()
+
+
+def _const(name):
+    return int(re.search(rf"constexpr int {name} = (\d+);", SRC).group(1))
+
+
+THREADS, PAD_PAIRS, FB = _const("kThreads"), _const("kPadPairs"), _const("kFB")
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def xcd_share(i, n):
+    """sdm_gather_kernel's token order: workgroup i (run on XCD i mod 8) takes the
+    i // 8-th of a contiguous eighth of the n (token block, slice) pairs."""
+    q, r, x, k = n // 8, n % 8, i % 8, i // 8
+    return x * q + min(x, r) + k
+
+
+@pytest.mark.parametrize("n", list(range(1, 70)) + [255, 256, 257, 4096, 4097, 8191])
+def test_xcd_share_is_a_bijection(n):
+    assert sorted(xcd_share(i, n) for i in range(n)) == list(range(n))
+
+
+def test_xcd_share_gives_each_xcd_a_contiguous_run():
+    n = 1000
+    for x in range(8):
+        got = sorted(xcd_share(i, n) for i in range(x, n, 8))
+        assert got == list(range(got[0], got[0] + len(got)))
+
+
+def wave_pair(i, gpw):
+    """sdm_gather_pair_kernel: live pair index -> (token-slice index, operand)."""
+    w = i // gpw
+    return (w >> 1) * gpw + (i - w * gpw), w & 1
+
+
+@pytest.mark.parametrize("gpw", [1, 2, 4])
+@pytest.mark.parametrize("live_ks", [0, 1, 3, 4, 5, 63, 64, 65, 1000])
+def test_wave_pairs_cover_each_pair_once_with_one_operand_per_wavefront(gpw, live_ks):
+    live_pairs = cdiv(live_ks, gpw) * 2 * gpw
+    seen = [wave_pair(i, gpw) for i in range(live_pairs)]
+    named = [s for s in seen if s[0] < live_ks]
+    assert sorted(named) == sorted((k, op) for k in range(live_ks) for op in (0, 1))
+    for w0 in range(0, live_pairs, gpw):  # a wavefront's groups: gpw consecutive indices
+        assert len({seen[i][1] for i in range(w0, w0 + gpw)}) == 1
+
+
+def pair_units(tokens, live, slices, nops, gpw):
+    """sdm_gather_pair_kernel: live pairs (whole runs for two operands) plus runs of
+    kPadPairs padding pairs."""
+    live_ks = live * slices
+    live_pairs = cdiv(live_ks, gpw) * 2 * gpw if nops == 2 else live_ks
+    return live_pairs + cdiv((tokens - live) * nops * slices, PAD_PAIRS)
+
+
+def pair_grid_units(tokens, slices, nops, lpr):
+    """launch_pair_typed: the grid, in lane-group units."""
+    groups, gpw, ks = THREADS // lpr, 64 // lpr, tokens * slices
+    pairs = cdiv(ks, gpw) * 2 * gpw if nops == 2 else ks
+    return cdiv(pairs + 2 * gpw, groups) * groups
+
+
+@pytest.mark.parametrize("nops", [1, 2])
+@pytest.mark.parametrize("slices", [1, 2, 3])
+def test_pair_grid_holds_every_liveness(nops, slices):
+    lpr = 16
+    gpw = 64 // lpr
+    for tokens in list(range(1, 300)) + [32767, 32768]:
+        cap = pair_grid_units(tokens, slices, nops, lpr)
+        lives = range(tokens + 1) if tokens < 300 else list(range(60)) + list(range(tokens - 60, tokens + 1))
+        for live in lives:
+            assert pair_units(tokens, live, slices, nops, gpw) <= cap, (tokens, live)
+
+
+def test_pair_batches_fit_a_group():
+    # lane l of a 16-lane group loads entry l mod kFB of each batch: a batch fits the group
+    assert 1 <= FB <= 16 and 16 % FB == 0
+
+
+class LiveMap:
+    """LiveMap: the live and padding tokens of a launch from its per-chunk counts."""
+
+    def __init__(self, counts, chunk):
+        self.chunk = chunk
+        self.pref = np.concatenate([[0], np.cumsum(np.clip(counts, 0, chunk))])
+        self.chunks = len(counts)
+
+    def live_at(self, j):
+        lo, hi = 0, self.chunks - 1
+        while lo < hi:
+            mid = (lo + hi + 1) // 2
+            if self.pref[mid] <= j:
+                lo = mid
+            else:
+                hi = mid - 1
+        return lo * self.chunk + (j - self.pref[lo])
+
+    def pad_token(self, j):
+        lo, hi = 0, self.chunks - 1
+        while lo < hi:
+            mid = (lo + hi + 1) // 2
+            if mid * self.chunk - self.pref[mid] <= j:
+                lo = mid
+            else:
+                hi = mid - 1
+        c = lo
+        return c * self.chunk + (self.pref[c + 1] - self.pref[c]) + (j - (c * self.chunk - self.pref[c]))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_live_map_lists_the_live_and_the_padding_tokens(seed):
+    rng = np.random.default_rng(seed)
+    chunk = int(rng.integers(1, 70))
+    chunks = int(rng.integers(1, 40))
+    counts = rng.integers(-3, chunk + 4, chunks)  # out-of-range counts are clamped
+    m = LiveMap(counts, chunk)
+    t = np.arange(chunks * chunk)
+    live = t % chunk < np.clip(counts, 0, chunk)[t // chunk]
+    assert [m.live_at(j) for j in range(int(m.pref[-1]))] == list(t[live])
+    assert [m.pad_token(j) for j in range(chunks * chunk - int(m.pref[-1]))] == list(t[~live])
