@@ -480,7 +480,6 @@ __device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_byte
 // units exit after the block's scan of the per-chunk counts.
 template <typename E, int VB, int NOPS, typename IdxT, typename WT>
 __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherParams p) {
-    using V = typename RawVec<VB>::T;
     constexpr int VEC = VB / int(sizeof(E));
     extern __shared__ __align__(16) char s_raw[];
     const int tid = threadIdx.x;
