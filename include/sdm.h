@@ -28,6 +28,7 @@ extern "C" {
 
 #define SDM_ABI_VERSION 3 /* 2: adds sdm_gather_compact and the gather plan; 3: sdm_round_bf16 */
 #define SDM_MAX_WIDTH 256 /* largest W, R and gather width */
+#define SDM_MAX_ROW_BYTES (1LL << 30) /* largest bank row, head_dim x element size, in bytes */
 
 /* Element types (sdm_dtype). */
 enum {
@@ -42,8 +43,9 @@ enum {
     SDM_OK = 0,
     SDM_E_DTYPE = 1,   /* an element type outside the ones an argument accepts */
     SDM_E_SHAPE = 2,   /* a size that is negative, zero where one is needed, or inconsistent */
-    SDM_E_RANGE = 3,   /* a width outside 1..SDM_MAX_WIDTH, a count outside its range, or a
-                          slot-list precondition broken (SDM_DEBUG_VALIDATE only) */
+    SDM_E_RANGE = 3,   /* a width outside 1..SDM_MAX_WIDTH, a bank row above SDM_MAX_ROW_BYTES,
+                          a count outside its range, or a slot-list precondition broken
+                          (SDM_DEBUG_VALIDATE only) */
     SDM_E_ALIGN = 4,   /* a pointer not aligned to its element size */
     SDM_E_OVERLAP = 5, /* an output overlapping the bank or another output */
     SDM_E_NULL = 6,    /* a required pointer is NULL (or operand 1 given in part) */
@@ -82,7 +84,7 @@ enum {
  * Arguments:
  *   bank        [num_slots, head_dim] of bank_dtype (SDM_F32 or SDM_BF16);
  *               read and written in place.
- *   num_slots   >= 1. head_dim >= 1.
+ *   num_slots   >= 1. head_dim >= 1, a row of at most SDM_MAX_ROW_BYTES.
  *   streams     >= 0; 0 enqueues nothing and returns SDM_OK.
  *   W, R        write and read widths, 1..SDM_MAX_WIDTH.
  *   G           1 (one gate per stream) or W (one gate per write).
@@ -163,7 +165,8 @@ int sdm_decode_steps(void* bank, int bank_dtype, int64_t num_slots, int64_t head
  * 1" order of the pages); it depends on nothing but the inputs.
  *
  * Arguments:
- *   bank         [num_slots, head_dim] of bank_dtype (SDM_F32 or SDM_BF16); read only.
+ *   bank         [num_slots, head_dim] of bank_dtype (SDM_F32 or SDM_BF16); read only;
+ *                num_slots, head_dim >= 1, a row of at most SDM_MAX_ROW_BYTES.
  *   tokens       >= 0, a multiple of chunk; 0 enqueues nothing and returns SDM_OK.
  *   chunk        >= 1.  valid in [0, chunk].
  *   chunk_valid  NULL, or [tokens / chunk] int32 on the device, each in [0, chunk]

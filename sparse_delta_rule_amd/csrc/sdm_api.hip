@@ -299,6 +299,9 @@ int decode_call(const char* fn, void* bank, int bank_dtype, int64_t num_slots, i
     if (num_slots < 1 || head_dim < 1)
         return fail(SDM_E_SHAPE, "%s: empty bank [%lld, %lld]: num_slots and head_dim must both be positive", fn,
                     (long long)num_slots, (long long)head_dim);
+    if (head_dim > SDM_MAX_ROW_BYTES / (bank_dtype == SDM_BF16 ? 2 : 4))
+        return fail(SDM_E_RANGE, "%s: head_dim %lld: a bank row would exceed %lld bytes", fn, (long long)head_dim,
+                    (long long)SDM_MAX_ROW_BYTES);
     if (streams < 0) return fail(SDM_E_SHAPE, "%s: streams = %lld < 0", fn, (long long)streams);
     if (steps < 0) return fail(SDM_E_SHAPE, "%s: steps = %lld < 0", fn, (long long)steps);
     if (W < 1 || W > SDM_MAX_WIDTH || R < 1 || R > SDM_MAX_WIDTH)
@@ -423,6 +426,9 @@ int gather_prepare(const char* fn, const void* bank, int bank_dtype, int64_t num
     if (num_slots < 1 || head_dim < 1)
         return fail(SDM_E_SHAPE, "%s: empty bank [%lld, %lld]: num_slots and head_dim must both be positive", fn,
                     (long long)num_slots, (long long)head_dim);
+    if (head_dim > SDM_MAX_ROW_BYTES / (bank_dtype == SDM_BF16 ? 2 : 4))
+        return fail(SDM_E_RANGE, "%s: head_dim %lld: a bank row would exceed %lld bytes", fn, (long long)head_dim,
+                    (long long)SDM_MAX_ROW_BYTES);
     if (tokens < 0 || chunk < 1 || tokens % chunk != 0 || valid < 0 || valid > chunk)
         return fail(SDM_E_SHAPE, "%s: tokens must be a whole number of chunks and valid lie in [0, chunk]: tokens=%lld "
                     "chunk=%lld valid=%lld", fn, (long long)tokens, (long long)chunk, (long long)valid);

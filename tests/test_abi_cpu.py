@@ -99,6 +99,8 @@ def call_decode(**kw):
     (dict(q_idx_dtype=BF16), E_DTYPE, "k_idx and q_idx"),
     (dict(num_slots=0), E_SHAPE, "empty bank"),
     (dict(head_dim=0), E_SHAPE, "empty bank"),
+    (dict(head_dim=(1 << 28) + 1, bank_dtype=F32), E_RANGE, "a bank row would exceed"),
+    (dict(head_dim=(1 << 29) + 1, bank_dtype=BF16), E_RANGE, "a bank row would exceed"),
     (dict(streams=-1), E_SHAPE, "streams"),
     (dict(W=0), E_RANGE, "each width must lie in 1..256"),
     (dict(W=257), E_RANGE, "each width must lie in 1..256"),
@@ -193,6 +195,8 @@ def call_gather(**kw):
     (dict(w_dtype=I32), E_DTYPE, "weights must be"),
     (dict(num_slots=0), E_SHAPE, "empty bank"),
     (dict(head_dim=0), E_SHAPE, "empty bank"),
+    (dict(head_dim=(1 << 28) + 1, bank_dtype=F32), E_RANGE, "a bank row would exceed"),
+    (dict(head_dim=(1 << 29) + 1, bank_dtype=BF16), E_RANGE, "a bank row would exceed"),
     (dict(tokens=-16), E_SHAPE, "whole number of chunks"),
     (dict(tokens=60), E_SHAPE, "whole number of chunks"),
     (dict(chunk=0), E_SHAPE, "whole number of chunks"),
@@ -283,6 +287,7 @@ def plan_launch(plan, row0, valid):
     (dict(bank_dtype=I64), E_DTYPE, "bank must be"),
     (dict(tokens=60), E_SHAPE, "whole number of chunks"),
     (dict(width0=0), E_RANGE, "width0"),
+    (dict(head_dim=(1 << 29) + 1, bank_dtype=BF16), E_RANGE, "a bank row would exceed"),
     (dict(idx1=None), E_NULL, "given in part"),
     (dict(out0=A + 1000 * 128), E_OVERLAP, "shares memory with the bank"),
     (dict(out1=A + 1200 * MB + 4096), E_OVERLAP, "the stash and the outputs share memory"),
