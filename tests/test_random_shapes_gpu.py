@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 # Cases per sweep; SDM_SWEEP_CASES=<n> runs a longer sweep (same seeds, more of them).
 N_CASES = int(os.environ.get("SDM_SWEEP_CASES", "0")) or None
 
-HEAD_DIMS = [1, 2, 3, 5, 8, 16, 31, 64, 100, 101, 127, 128, 129, 200, 255, 256, 300, 512, 700]
+HEAD_DIMS = [1, 2, 3, 5, 8, 16, 31, 36, 64, 72, 100, 101, 120, 127, 128, 129, 200, 255, 256, 300, 512, 700]
 WIDTHS = [1, 2, 3, 4, 5, 7, 8, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256]
 
 
@@ -71,10 +71,12 @@ def _gather_case(i):
 
 @pytest.mark.parametrize("i", range(N_CASES or 64))
 def test_random_gather_shapes(i):
-    """The gather (with and without the stash, per-chunk or scalar valid) and the
-    compact-stash gather on a random shape equal the oracle."""
+    """The gather (with and without the stash, per-chunk or scalar valid; rows of
+    9 to 16 vectors take the pair layout without it) and the compact-stash gather on
+    a random shape equal the oracle."""
     wl = _gather_case(i)
     print(wl, flush=True)
     run_case(wl, 40 + i, per_chunk=True)
+    run_case(wl, 40 + i, per_chunk=True, stash=False)
     run_case(wl, 40 + i, per_chunk=False, valid=wl.chunk // 2, stash=False)
     run_compact(wl, 40 + i)
