@@ -30,11 +30,11 @@
 // row p of its chunk's block of chunk * width0 rows instead of at (t, n); other
 // entries and padding tokens store nothing.
 //
-// Launches without a stash whose rows are 16 lane-vectors wide take the pair
-// layout instead (sdm_gather_pair_kernel, described where it is defined): no
-// LDS staging, the slots passed round a 16-lane group by DPP row broadcasts, few
-// registers and so more wavefronts in flight. Which layout runs changes no bit
-// of any result.
+// Launches without a stash whose rows are at least 9 lane-vectors wide take the
+// pair layout instead (sdm_gather_pair_kernel, described where it is defined):
+// no LDS staging, the slots passed round a lane group of 16, 32 or 64 lanes by
+// cross-lane moves, few registers and so more wavefronts in flight. Which layout
+// runs changes no bit of any result.
 
 #include "sdm_kernels.h"
 
@@ -375,39 +375,51 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     }
 }
 
-// Pair layout, for launches without a stash and rows of 9 to 16 lane-vectors
-// (16-lane groups): each group takes one (token, operand) pair, the live pairs
-// first (in the order of the live tokens, the groups of one wavefront on one
-// operand), then runs of kPadPairs padding pairs, whose outputs are +0. A pair's
-// entries are taken in ascending batches of kFB: lane l of the group requests the
-// slot and weight of entry l mod kFB of the next batch before this batch's rows
-// and the group passes them round with DPP row broadcasts (a 16-lane group is a
-// DPP row), so each batch costs one memory round trip and the slots never pass
+// Pair layout, for launches without a stash and rows of at least 9 lane-vectors
+// (lane groups of 16, 32 or 64 lanes): each group takes one (token, operand,
+// slice) pair, the live pairs first (in the order of the live tokens, the groups
+// of one wavefront on one operand), then runs of kPadPairs padding pairs, whose
+// outputs are +0. A pair's entries are taken in ascending batches of kFB: lane l
+// of the group requests the slot and weight of entry l mod kFB of the next batch
+// before this batch's rows, and the group passes them round by cross-lane moves
+// that need no LDS round trip (DPP row broadcasts for 16-lane groups, which are
+// DPP rows; reads of one lane into a scalar register for 32- and 64-lane
+// groups), so each batch costs one memory round trip and the slots never pass
 // through LDS; with no staging and no stash the kernel keeps few registers, so
 // eight wavefronts per SIMD (more rows) are in flight. The same lanes, vectors
 // and fused multiply-add chain as the token-order layout: the same bits.
 constexpr int kFB = 8;
 constexpr int kPadPairs = 8;
 
-// Lane I's value of a register within each row of 16 lanes (DPP's row
-// broadcast: a VALU move, no LDS round trip); 16-, 32- or 64-bit values.
-template <int I> __device__ __forceinline__ uint32_t row_lane(uint32_t v) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x150 + I, 0xf, 0xf, false));
+// Lane I of its group's value of a register, for lane groups of LPR lanes: a DPP
+// row broadcast for 16-lane groups (a DPP row is 16 lanes), the lane read into a
+// scalar register for 64-lane groups, and for 32-lane groups both halves' lanes
+// read and each half taking its own; 16-, 32- or 64-bit values.
+template <int LPR, int I> __device__ __forceinline__ uint32_t row_lane(uint32_t v) {
+    if constexpr (LPR == 16) {
+        return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x150 + I, 0xf, 0xf, false));
+    } else if constexpr (LPR == 64) {
+        return uint32_t(__builtin_amdgcn_readlane(int(v), I));
+    } else {
+        const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(v), I));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(v), 32 + I));
+        return (threadIdx.x & 32) ? hi : lo;
+    }
 }
-template <int I, typename T> __device__ __forceinline__ T bcast(T v) {
+template <int LPR, int I, typename T> __device__ __forceinline__ T bcast(T v) {
     if constexpr (sizeof(T) == 8) {
         const uint64_t x = uint64_t(v);
-        const uint64_t lo = row_lane<I>(uint32_t(x)), hi = row_lane<I>(uint32_t(x >> 32));
+        const uint64_t lo = row_lane<LPR, I>(uint32_t(x)), hi = row_lane<LPR, I>(uint32_t(x >> 32));
         return T(lo | (hi << 32));
     } else if constexpr (sizeof(T) == 4) {
         uint32_t x;
         __builtin_memcpy(&x, &v, 4);
-        x = row_lane<I>(x);
+        x = row_lane<LPR, I>(x);
         T r;
         __builtin_memcpy(&r, &x, 4);
         return r;
     } else {
-        return T(row_lane<I>(uint32_t(v)));
+        return T(row_lane<LPR, I>(uint32_t(v)));
     }
 }
 
@@ -432,7 +444,7 @@ __device__ __forceinline__ int64_t wave_pair(int64_t i, int gpw, int& op) {
 // One pair's entries [0, width): see the pair layout above. Entries past the
 // width repeat entry width - 1 (the same row) and feed no sum. lane_row: this
 // lane's vector of bank row 0; row_bytes: a row's bytes.
-template <typename E, int VB, typename IdxT, typename WT>
+template <typename E, int VB, int LPR, typename IdxT, typename WT>
 __device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_bytes, const IdxT* idx, const WT* wts,
                                          int width, int lane, float (&acc)[VB / sizeof(E)]) {
     using V = typename RawVec<VB>::T;
@@ -443,7 +455,7 @@ __device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_byte
     WT mw = wts[e0];
     opaque(mw);  // waited for here, with the slot, not at the loop's top
     U sl[kFB];
-    static_for<kFB>([&](auto i) { sl[i] = U(bcast<i>(ms0)); });
+    static_for<kFB>([&](auto i) { sl[i] = U(bcast<LPR, i>(ms0)); });
     for (int n0 = 0; n0 < width; n0 += kFB) {
         // the next batch's slot and weight (this batch's again past the end)
         const int nx = n0 + kFB < width ? n0 + kFB : n0;
@@ -462,7 +474,7 @@ __device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_byte
         mw = mw_next;
         static_for<kFB>([&](auto i) {
             const bool use = n0 + i < width;
-            const float x = value_of<WT>(bcast<i>(wcur));
+            const float x = value_of<WT>(bcast<LPR, i>(wcur));
             E el[VEC];
             __builtin_memcpy(el, &r[i], VB);
 #pragma unroll
@@ -471,14 +483,14 @@ __device__ __forceinline__ void pair_sum(const char* lane_row, uint32_t row_byte
                 acc[k] = use ? term : acc[k];
             }
         });
-        static_for<kFB>([&](auto i) { sl[i] = U(bcast<i>(ms_next)); });
+        static_for<kFB>([&](auto i) { sl[i] = U(bcast<LPR, i>(ms_next)); });
     }
 }
 
 // One work unit (a live pair or a padding run) per lane group; the host sizes the
 // grid for the most units any liveness can give, and groups past the launch's
 // units exit after the block's scan of the per-chunk counts.
-template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+template <typename E, int VB, int NOPS, int LPR, typename IdxT, typename WT>
 __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherParams p) {
     constexpr int VEC = VB / int(sizeof(E));
     extern __shared__ __align__(16) char s_raw[];
@@ -562,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
         const WT* wts = static_cast<const WT*>(op == 0 ? p.w0 : p.w1) + t * width;
         const char* lane_row = reinterpret_cast<const char*>(bank + col);
         const uint32_t row_bytes = uint32_t(p.hd * int64_t(sizeof(E)));
-        pair_sum<E, VB>(lane_row, row_bytes, idx, wts, width, lane, acc);
+        pair_sum<E, VB, LPR>(lane_row, row_bytes, idx, wts, width, lane, acc);
         if (vi < p.vpr) store_out((op == 0 ? p.out0 : p.out1) + t * p.hd + col, acc);
     } else {
         // a run of padding pairs: operand-major, then token, then slice
@@ -577,8 +589,8 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
     }
 }
 
-template <typename E, int VB, int NOPS, typename IdxT, typename WT>
-hipError_t launch_pair_typed(const GatherParams& p, hipStream_t stream) {
+template <typename E, int VB, int NOPS, int LPR, typename IdxT, typename WT>
+hipError_t launch_pair_lpr(const GatherParams& p, hipStream_t stream) {
     // the live pairs of every token live, rounded up to whole runs, plus gpw: the
     // most work units a launch can hold (a padding run of kPadPairs pairs stands
     // for fewer live pairs than it replaces, but a last run of live pairs rounded
@@ -587,9 +599,18 @@ hipError_t launch_pair_typed(const GatherParams& p, hipStream_t stream) {
     const int64_t pairs = NOPS == 2 ? (ks + gpw - 1) / gpw * (2 * gpw) : ks;
     const int64_t blocks = (pairs + gpw + groups - 1) / groups;
     const size_t lds = p.chunk_valid ? size_t(p.tokens / p.chunk + 1 + kThreads / 64) * 4 : 0;
-    hipLaunchKernelGGL((sdm_gather_pair_kernel<E, VB, NOPS, IdxT, WT>), dim3(unsigned(blocks)), dim3(kThreads), lds,
-                       stream, p);
+    hipLaunchKernelGGL((sdm_gather_pair_kernel<E, VB, NOPS, LPR, IdxT, WT>), dim3(unsigned(blocks)), dim3(kThreads),
+                       lds, stream, p);
     return hipGetLastError();
+}
+
+// Lane groups of 16, 32 or 64 lanes, each its own kernel (registers allocated for
+// its own broadcasts).
+template <typename E, int VB, int NOPS, typename IdxT, typename WT>
+hipError_t launch_pair_typed(const GatherParams& p, hipStream_t stream) {
+    if (p.lpr == 16) return launch_pair_lpr<E, VB, NOPS, 16, IdxT, WT>(p, stream);
+    if (p.lpr == 32) return launch_pair_lpr<E, VB, NOPS, 32, IdxT, WT>(p, stream);
+    return launch_pair_lpr<E, VB, NOPS, 64, IdxT, WT>(p, stream);
 }
 
 template <typename E, int VB, int NOPS>
@@ -631,7 +652,7 @@ hipError_t launch_live(const GatherParams& p, const GatherGeometry& geo, hipStre
 template <typename E, int VB, int NOPS, bool CMP>
 hipError_t launch_ops(const GatherParams& p, const GatherGeometry& geo, hipStream_t stream) {
     if constexpr (!CMP) {
-        if (p.stash == nullptr && p.lpr == 16 && (p.chunk_valid == nullptr || p.tokens / p.chunk <= kLiveMaxChunks))
+        if (p.stash == nullptr && p.lpr >= 16 && (p.chunk_valid == nullptr || p.tokens / p.chunk <= kLiveMaxChunks))
             return launch_pair<E, VB, NOPS>(p, stream);
     }
     const bool full_stash = p.stash != nullptr && !CMP;

@@ -78,8 +78,8 @@ def pair_grid_units(tokens, slices, nops, lpr):
 
 @pytest.mark.parametrize("nops", [1, 2])
 @pytest.mark.parametrize("slices", [1, 2, 3])
-def test_pair_grid_holds_every_liveness(nops, slices):
-    lpr = 16
+@pytest.mark.parametrize("lpr", [16, 32, 64])
+def test_pair_grid_holds_every_liveness(nops, slices, lpr):
     gpw = 64 // lpr
     for tokens in list(range(1, 300)) + [32767, 32768]:
         cap = pair_grid_units(tokens, slices, nops, lpr)
@@ -89,8 +89,10 @@ def test_pair_grid_holds_every_liveness(nops, slices):
 
 
 def test_pair_batches_fit_a_group():
-    # lane l of a 16-lane group loads entry l mod kFB of each batch: a batch fits the group
+    # lane l of a group (16 lanes or more) loads entry l mod kFB of each batch: a
+    # batch fits the smallest group
     assert 1 <= FB <= 16 and 16 % FB == 0
+    assert re.search(r"p\.lpr >= 16 &&", SRC), "the pair layout takes groups of 16 lanes or more"
 
 
 class LiveMap:
