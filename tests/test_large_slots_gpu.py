@@ -91,6 +91,15 @@ def test_gather_pair_layout_slots_past_2_31():
     torch.cuda.empty_cache()
 
 
+def test_gather_pair_layout_32_lane_groups_slots_past_2_31():
+    """Rows of seventeen bfloat16 elements (17 two-byte vectors: 32-lane groups, whose
+    slots are read into scalar registers, 64-bit here) and no stash (a 73 GB bank)."""
+    bank = torch.zeros((ROWS, 17), dtype=torch.bfloat16, device=DEV)
+    gather_past_2_31(bank, with_stash=False)
+    del bank
+    torch.cuda.empty_cache()
+
+
 def gather_past_2_31(bank, with_stash):
     hd = bank.shape[1]
     rng = np.random.default_rng(32)
