@@ -70,10 +70,14 @@ def pair_units(tokens, live, slices, nops, gpw):
 
 
 def pair_grid_units(tokens, slices, nops, lpr):
-    """launch_pair_typed: the grid, in lane-group units."""
+    """launch_pair_lpr: the grid, in lane-group units."""
     groups, gpw, ks = THREADS // lpr, 64 // lpr, tokens * slices
     pairs = cdiv(ks, gpw) * 2 * gpw if nops == 2 else ks
-    return cdiv(pairs + 2 * gpw, groups) * groups
+    return cdiv(pairs + gpw, groups) * groups
+
+
+def test_the_grid_formula_is_the_launchs():
+    assert "const int64_t blocks = (pairs + gpw + groups - 1) / groups;" in SRC
 
 
 @pytest.mark.parametrize("nops", [1, 2])
