@@ -76,8 +76,15 @@ def pair_grid_units(tokens, slices, nops, lpr):
     return cdiv(pairs + gpw, groups) * groups
 
 
-def test_the_grid_formula_is_the_launchs():
-    assert "const int64_t blocks = (pairs + gpw + groups - 1) / groups;" in SRC
+def test_the_restated_formulas_are_the_kernels():
+    """Each restated formula, as it stands in the kernel source."""
+    for line in ("const int64_t blocks = (pairs + gpw + groups - 1) / groups;",
+                 "const int64_t live_pairs = NOPS == 2 ? (live_ks + gpw - 1) / gpw * (2 * gpw) : live_ks;",
+                 "pad_runs = (pad_pairs + kPadPairs - 1) / kPadPairs;",
+                 "const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;",
+                 "const int64_t j = x * q + (x < r ? x : r) + k;",
+                 "return (w >> 1) * gpw + (i - w * gpw);"):
+        assert line in SRC, line
 
 
 @pytest.mark.parametrize("nops", [1, 2])
