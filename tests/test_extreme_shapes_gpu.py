@@ -40,6 +40,8 @@ GATHER = [
     ("one chunk of every token", torch.bfloat16, 3000, 128, 200, 200, 32, 32),
     ("chunks of one token", torch.bfloat16, 3000, 128, 150, 1, 16, 8),
     ("hd 1, widths 256", torch.float32, 1000, 1, 40, 8, 256, 256),
+    # past the 4096 chunks a workgroup's LDS scan takes: the token-order layout
+    ("5000 chunks of one token", torch.bfloat16, 3000, 128, 5000, 1, 8, 4),
 ]
 
 
@@ -52,4 +54,6 @@ def test_gather_extremes(case):
     print(name, flush=True)
     run_case(wl, 62, per_chunk=True)
     run_case(wl, 62, per_chunk=False, valid=max(1, chunk - 1))
+    run_case(wl, 62, per_chunk=True, stash=False)
+    run_case(wl, 62, per_chunk=False, valid=max(1, chunk - 1), stash=False)
     run_compact(wl, 62)
