@@ -166,6 +166,10 @@ def parse_args(argv=None):
                    help="summarise rocprofv3 output of one --ceiling run (one bank size) into profiles/ (no GPU)")
     p.add_argument("--tokens", type=int, default=None,
                    help="gather: launch over this many tokens (a multiple of the chunk) instead of the workload's")
+    p.add_argument("--head-dim", type=int, default=None,
+                   help="gather: bank rows of this many elements instead of the workload's (same slots and tokens)")
+    p.add_argument("--bank-dtype", choices=["bf16", "f32"], default=None,
+                   help="gather: bank element type instead of the workload's")
     p.add_argument("--valid", default="per-chunk",
                    help="gather: per-chunk (the workload's per-chunk counts), all (every token live, no counts) "
                         "or N (one count N for every chunk, passed as the scalar valid)")
@@ -513,11 +517,17 @@ def bench_gather(torch, args, cfg_name, wl):
     import gen
     from sparse_delta_rule_amd import sdm_gather, sdm_gather_compact
     dev = torch.device("cuda", 0)
-    es = torch.empty((), dtype=wl.bank_dtype).element_size()
     if args.tokens is not None:
         if args.tokens < wl.chunk or args.tokens % wl.chunk:
             raise SystemExit("bench.py: --tokens must be a positive multiple of the chunk")
         wl = wl.replace(tokens=args.tokens)
+    if args.head_dim is not None:
+        if args.head_dim < 1:
+            raise SystemExit("bench.py: --head-dim must be positive")
+        wl = wl.replace(head_dim=args.head_dim)
+    if args.bank_dtype is not None:
+        wl = wl.replace(bank_dtype={"bf16": torch.bfloat16, "f32": torch.float32}[args.bank_dtype])
+    es = torch.empty((), dtype=wl.bank_dtype).element_size()
     bank = gen.gather_bank(wl, args.seed, dev)
     inp = gen.gather_inputs(wl, args.seed, dev)
     T = wl.tokens
@@ -568,6 +578,8 @@ def bench_gather(torch, args, cfg_name, wl):
     name = f"{cfg_name}: {wl.name}" + ("" if args.gather == "two-ops" else f" [{args.gather}]")
     if args.tokens is not None or args.valid != "per-chunk":
         name += f" [{T} tokens, valid {args.valid}]"
+    if args.head_dim is not None or args.bank_dtype is not None:
+        name += f" [head_dim {wl.head_dim}, {str(wl.bank_dtype).replace('torch.', '')} bank]"
     config = {"workload": name, "tokens": T, "live_tokens": live, "valid": args.valid, "chunk": wl.chunk,
               "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0],
               "stash": "compact" if compact else with_stash, "stash_rows": stash_rows,
@@ -862,7 +874,8 @@ def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0, gather: str = "t
 
 def ingest_profile(args) -> int:
     trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
-    if args.config == "c3" and (args.gather not in GATHER_SHAPES or args.valid != "per-chunk" or args.tokens):
+    if args.config == "c3" and (args.gather not in GATHER_SHAPES or args.valid != "per-chunk" or args.tokens
+                                or args.head_dim is not None or args.bank_dtype is not None):
         raise SystemExit("bench.py: gather profiles are summarised for c3's own tokens and per-chunk counts, "
                          f"in the launch shapes {sorted(GATHER_SHAPES)}")
     kind = launch_kind(args.config, args.entry, args.gather)
@@ -1083,6 +1096,8 @@ def ingest_ceiling(args) -> int:
 
 def main(argv=None):
     args = parse_args(argv)
+    if (args.head_dim is not None or args.bank_dtype is not None) and args.config != "c3":
+        raise SystemExit("bench.py: --head-dim and --bank-dtype change the gather's bank (--config c3)")
     if args.ingest_profile:
         sys.path.insert(0, ROOT)
         return ingest_profile(args)
@@ -1136,6 +1151,8 @@ def main_one(torch, gen, args, wl) -> int:
         r = bench_gather(torch, args, args.config, wl)
     kind = launch_kind(args.config, args.entry, args.gather)
     traffic, kernel = stored_traffic(args.config, kind, r["tokens_per_launch"], r["live_tokens"])
+    if getattr(args, "head_dim", None) is not None or getattr(args, "bank_dtype", None) is not None:
+        traffic, kernel = None, None  # the stored figures are for the workload's own rows
     copy_gbps = streaming_copy_gbps(torch)
     out = {
         "metric": METRIC,

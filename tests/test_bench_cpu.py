@@ -363,3 +363,15 @@ def test_stream_sweep_fit(tmp_path, monkeypatch):
     assert "marginal rate of 4915 GB/s" in md
     with pytest.raises(SystemExit, match="--streams list"):
         bench.main(["--config", "c2", "--entry", "step", "--streams", "512,1024", "--ingest-stream-sweep", str(d)])
+
+
+def test_gather_bank_overrides_are_for_the_gather_and_never_profiled(tmp_path, monkeypatch):
+    with pytest.raises(SystemExit, match="--config c3"):
+        bench.main(["--config", "c2", "--head-dim", "256"])
+    with pytest.raises(SystemExit, match="--config c3"):
+        bench.main(["--config", "c1", "--bank-dtype", "f32"])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    for flags in (["--head-dim", "256"], ["--bank-dtype", "f32"]):
+        with pytest.raises(SystemExit, match="c3's own tokens"):
+            bench.main(["--config", "c3", *flags, "--ingest-profile", t, f, w, cf, cw])
