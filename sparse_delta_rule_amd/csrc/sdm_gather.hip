@@ -377,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
 
 // Pair layout, for launches without a stash and rows of at least 9 lane-vectors
 // (lane groups of 16, 32 or 64 lanes): each group takes one (token, operand,
-// slice) pair, the live pairs first (in the order of the live tokens, the groups
-// of one wavefront on one operand), then runs of kPadPairs padding pairs, whose
+// slice) pair, the live pairs first (operand 0's, then operand 1's, each in the
+// order of the live tokens and in whole wavefronts), then runs of kPadPairs padding pairs, whose
 // outputs are +0. A pair's entries are taken in ascending batches of kFB: lane l
 // of the group requests the slot and weight of entry l mod kFB of the next batch
 // before this batch's rows, and the group passes them round by cross-lane moves
@@ -432,13 +432,18 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Live pair index i -> (the pair's (token, slice) index k, operand): with two
-// operands, runs of gpw groups (one wavefront) alternate between the operands,
-// so the operand is uniform over a wavefront; indices k >= n (the live tokens
-// times the slices) name no pair (a last, partial run).
-__device__ __forceinline__ int64_t wave_pair(int64_t i, int gpw, int& op) {
-    const int64_t w = i / gpw;
-    op = int(w & 1);
-    return (w >> 1) * gpw + (i - w * gpw);
+// operands, operand 0's pairs take the first run = ceil(n / gpw) * gpw indices
+// (whole wavefronts) and operand 1's the next run, so the operand is uniform over a
+// wavefront; indices k >= n (the live tokens times the slices) name no pair (the
+// end of a run). Operand-major, not interleaved by wavefront: the wavefronts in
+// flight then store rows of one output that follow one another, never the same
+// token's rows of both outputs at once. Two outputs allocated back to back lie a
+// power of two apart whenever the token count is one, and such paired stores
+// measured 9 % slower at 32768 tokens of 512-byte output rows (1 % slower shifted
+// by a few KiB, and no slower shifted by 1 MiB): they collide in the memory.
+__device__ __forceinline__ int64_t operand_pair(int64_t i, int64_t run, int& op) {
+    op = i >= run ? 1 : 0;
+    return op ? i - run : i;
 }
 
 // One pair's entries [0, width): see the pair layout above. Entries past the
@@ -542,7 +547,8 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
     const int gpw = 64 / p.lpr;
     // live pair indices: whole pairs of runs for two operands
     const int64_t live_ks = live * slices;
-    const int64_t live_pairs = NOPS == 2 ? (live_ks + gpw - 1) / gpw * (2 * gpw) : live_ks;
+    const int64_t live_run = (live_ks + gpw - 1) / gpw * gpw;  // one operand's live pairs, whole wavefronts
+    const int64_t live_pairs = NOPS == 2 ? 2 * live_run : live_ks;
     const int64_t pad_pairs = pads * NOPS * slices, pad_runs = (pad_pairs + kPadPairs - 1) / kPadPairs;
     const int64_t u = int64_t(blockIdx.x) * groups + tid / p.lpr;
     if (u >= live_pairs + pad_runs) return;
@@ -563,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
     if (u < live_pairs) {
         int op = 0;
-        const int64_t k = NOPS == 2 ? wave_pair(u, gpw, op) : u;
+        const int64_t k = NOPS == 2 ? operand_pair(u, live_run, op) : u;
         if (k >= live_ks) return;
         op = __builtin_amdgcn_readfirstlane(op);  // uniform over the wavefront (whole runs)
         const int64_t t = m.live_at(k / slices);

@@ -44,28 +44,42 @@ def test_xcd_share_gives_each_xcd_a_contiguous_run():
         assert got == list(range(got[0], got[0] + len(got)))
 
 
-def wave_pair(i, gpw):
-    """sdm_gather_pair_kernel: live pair index -> (token-slice index, operand)."""
-    w = i // gpw
-    return (w >> 1) * gpw + (i - w * gpw), w & 1
+def operand_pair(i, run):
+    """sdm_gather_pair_kernel: live pair index -> (token-slice index, operand), operand 0's
+    run of indices first."""
+    op = 1 if i >= run else 0
+    return (i - run if op else i), op
 
 
 @pytest.mark.parametrize("gpw", [1, 2, 4])
 @pytest.mark.parametrize("live_ks", [0, 1, 3, 4, 5, 63, 64, 65, 1000])
-def test_wave_pairs_cover_each_pair_once_with_one_operand_per_wavefront(gpw, live_ks):
-    live_pairs = cdiv(live_ks, gpw) * 2 * gpw
-    seen = [wave_pair(i, gpw) for i in range(live_pairs)]
+def test_operand_pairs_cover_each_pair_once_with_one_operand_per_wavefront(gpw, live_ks):
+    run = cdiv(live_ks, gpw) * gpw
+    live_pairs = 2 * run
+    seen = [operand_pair(i, run) for i in range(live_pairs)]
     named = [s for s in seen if s[0] < live_ks]
     assert sorted(named) == sorted((k, op) for k in range(live_ks) for op in (0, 1))
     for w0 in range(0, live_pairs, gpw):  # a wavefront's groups: gpw consecutive indices
         assert len({seen[i][1] for i in range(w0, w0 + gpw)}) == 1
 
 
+@pytest.mark.parametrize("gpw", [1, 2, 4])
+def test_operand_pairs_never_hold_one_token_of_both_operands_in_a_window(gpw):
+    # operand-major: a window of consecutive indices (the wavefronts in flight) shorter
+    # than one operand's run never holds one token's pairs of both operands
+    live_ks = 5000
+    run = cdiv(live_ks, gpw) * gpw
+    window = 1024
+    for w0 in range(0, 2 * run - window, 97):
+        got = [operand_pair(i, run) for i in range(w0, w0 + window)]
+        assert not {k for k, op in got if op == 0} & {k for k, op in got if op == 1}, w0
+
+
 def pair_units(tokens, live, slices, nops, gpw):
     """sdm_gather_pair_kernel: live pairs (whole runs for two operands) plus runs of
     kPadPairs padding pairs."""
     live_ks = live * slices
-    live_pairs = cdiv(live_ks, gpw) * 2 * gpw if nops == 2 else live_ks
+    live_pairs = 2 * cdiv(live_ks, gpw) * gpw if nops == 2 else live_ks
     return live_pairs + cdiv((tokens - live) * nops * slices, PAD_PAIRS)
 
 
@@ -79,11 +93,13 @@ def pair_grid_units(tokens, slices, nops, lpr):
 def test_the_restated_formulas_are_the_kernels():
     """Each restated formula, as it stands in the kernel source."""
     for line in ("const int64_t blocks = (pairs + gpw + groups - 1) / groups;",
-                 "const int64_t live_pairs = NOPS == 2 ? (live_ks + gpw - 1) / gpw * (2 * gpw) : live_ks;",
+                 "const int64_t live_run = (live_ks + gpw - 1) / gpw * gpw;",
+                 "const int64_t live_pairs = NOPS == 2 ? 2 * live_run : live_ks;",
                  "pad_runs = (pad_pairs + kPadPairs - 1) / kPadPairs;",
                  "const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;",
                  "const int64_t j = x * q + (x < r ? x : r) + k;",
-                 "return (w >> 1) * gpw + (i - w * gpw);"):
+                 "op = i >= run ? 1 : 0;",
+                 "return op ? i - run : i;"):
         assert line in SRC, line
 
 
