@@ -104,6 +104,22 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     }
 }
 
+// Inclusive sum over a wavefront's 64 lanes: DPP shifts right by 1, 2, 4 and 8
+// lanes within each row of 16 lanes (a lane whose source lies outside its row adds
+// 0), then each row adds the totals of the rows before it, read from lanes 15, 31
+// and 47 into scalar registers.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    const int32_t r0 = __builtin_amdgcn_readlane(x, 15);
+    const int32_t r1 = r0 + __builtin_amdgcn_readlane(x, 31);
+    const int32_t r2 = r1 + __builtin_amdgcn_readlane(x, 47);
+    const int row = int(threadIdx.x & 63) >> 4;
+    return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r1 : r2);
+}
+
 // Live-token layout (LIVE): token block b takes live tokens [b tpb, b tpb + tpb)
 // of the L live tokens in order (chunk by chunk, each chunk's live positions), so
 // every block but the last is full of live tokens, and then writes the outputs
@@ -197,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
         int64_t live_total;
         if (p.chunk_valid != nullptr) {
             // exclusive prefix of the clamped counts: each thread sums a run of chunks,
-            // the runs are scanned within each wavefront (shuffles) and across the
+            // the runs are scanned within each wavefront (DPP and lane reads) and across the
             // wavefronts (LDS); then each thread fills in its run and places the
             // block's live tokens that fall in its chunks
             const int64_t per = (m.chunks + kThreads - 1) / kThreads, c0 = tid * per;
@@ -209,11 +225,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
                 run += n;
             }
             const int wl = tid & 63, wave = tid >> 6;
-            int32_t x = run;
-            for (int d = 1; d < 64; d *= 2) {
-                const int32_t y = __shfl_up(x, d);
-                x += wl >= d ? y : 0;
-            }
+            const int32_t x = wave_inclusive_sum(run);
             int32_t* s_wave = s_pref + m.chunks + 1;  // [kThreads / 64] wavefront totals
             if (wl == 63) s_wave[wave] = x;
             __syncthreads();  // (also orders the s_tok defaults before the placements below)
@@ -446,6 +458,30 @@ __device__ __forceinline__ int64_t operand_pair(int64_t i, int64_t run, int& op)
     return op ? i - run : i;
 }
 
+// LiveMap::live_at for the LPR lanes of one group, which share j: each step splits
+// the remaining chunks into LPR parts of step chunks, lane l tests whether part
+// l + 1 starts at or below j, and since the prefix never decreases the lanes that
+// pass are lanes 0 .. n - 1, so their count n (a ballot) names the part that
+// holds j. A probe past the remaining range fails (j lies before it), so each step
+// keeps a whole part: 512 chunks take 3 dependent LDS reads (16 lanes) or 2 (32
+// and 64) before the last, against 9 for a binary search.
+template <int LPR>
+__device__ __forceinline__ int64_t group_live_at(const LiveMap& m, int64_t j, int lane) {
+    if (m.pref == nullptr) return m.live_token(j);
+    const int shift = int(threadIdx.x & 63) & ~(LPR - 1);  // the group's first lane in the wavefront
+    int32_t lo = 0, n = int32_t(m.chunks);
+    while (n > 1) {  // the same steps for every group (they depend on the chunk count only)
+        const int32_t step = (n + LPR - 1) / LPR;
+        const int32_t probe = lo + (lane + 1) * step;
+        const bool pass = probe < m.chunks && m.pref[probe] <= j;
+        uint64_t b = __ballot(pass) >> shift;
+        if (LPR < 64) b &= (uint64_t(1) << LPR) - 1;
+        lo += int32_t(__popcll(b)) * step;
+        n = step;
+    }
+    return int64_t(lo) * m.chunk + (j - m.pref[lo]);
+}
+
 // One pair's entries [0, width): see the pair layout above. Entries past the
 // width repeat entry width - 1 (the same row) and feed no sum. lane_row: this
 // lane's vector of bank row 0; row_bytes: a row's bytes.
@@ -511,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
     m.pref = nullptr;
     if (p.chunk_valid != nullptr) {
         // exclusive prefix of the clamped per-chunk counts (runs of chunks per
-        // thread, scanned by shuffles within a wavefront and through LDS across them)
+        // thread, scanned by DPP within a wavefront and through LDS across them)
         int32_t* s_pref = reinterpret_cast<int32_t*>(s_raw);
         const int64_t per = (m.chunks + kThreads - 1) / kThreads, c0 = tid * per;
         int32_t run = 0;
@@ -522,11 +558,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
             run += n;
         }
         const int wl = tid & 63, wave = tid >> 6;
-        int32_t x = run;
-        for (int d = 1; d < 64; d *= 2) {
-            const int32_t y = __shfl_up(x, d);
-            x += wl >= d ? y : 0;
-        }
+        const int32_t x = wave_inclusive_sum(run);
         int32_t* s_wave = s_pref + m.chunks + 1;  // [kThreads / 64] wavefront totals
         if (wl == 63) s_wave[wave] = x;
         __syncthreads();
@@ -572,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
         const int64_t k = NOPS == 2 ? operand_pair(u, live_run, op) : u;
         if (k >= live_ks) return;
         op = __builtin_amdgcn_readfirstlane(op);  // uniform over the wavefront (whole runs)
-        const int64_t t = m.live_at(k / slices);
+        const int64_t t = group_live_at<LPR>(m, k / slices, lane);
         const int vi = int(k % slices) * p.lpr + lane;
         const int64_t col = int64_t(vi < p.vpr ? vi : p.vpr - 1) * VEC;
         const int width = op == 0 ? p.width0 : p.width1;

@@ -163,3 +163,74 @@ def test_live_map_lists_the_live_and_the_padding_tokens(seed):
     live = t % chunk < np.clip(counts, 0, chunk)[t // chunk]
     assert [m.live_at(j) for j in range(int(m.pref[-1]))] == list(t[live])
     assert [m.pad_token(j) for j in range(chunks * chunk - int(m.pref[-1]))] == list(t[~live])
+
+
+def wave_inclusive_sum(x):
+    """wave_inclusive_sum: DPP row_shr 1, 2, 4, 8 within rows of 16 lanes (a source
+    outside the row gives 0), then the earlier rows' totals from lanes 15, 31, 47."""
+    x = list(x)
+    for d in (1, 2, 4, 8):
+        x = [x[i] + (x[i - d] if i % 16 >= d else 0) for i in range(64)]
+    r0 = x[15]
+    r1 = r0 + x[31]
+    r2 = r1 + x[47]
+    return [x[i] + (0, r0, r1, r2)[i // 16] for i in range(64)]
+
+
+def test_wave_inclusive_sum_is_the_prefix_sum():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        x = rng.integers(0, 1 << 16, 64).tolist()
+        assert wave_inclusive_sum(x) == np.cumsum(x).tolist()
+    assert wave_inclusive_sum([1] * 64) == list(range(1, 65))
+
+
+def group_live_at(pref, chunks, chunk, j, lpr):
+    """group_live_at: the group's lanes split the remaining chunks into lpr parts a
+    step; the count of lanes whose part starts at or below j names the part."""
+    lo, n = 0, chunks
+    while n > 1:
+        step = -(-n // lpr)
+        passed = [lo + (lane + 1) * step < chunks and pref[lo + (lane + 1) * step] <= j for lane in range(lpr)]
+        assert passed == sorted(passed, reverse=True)  # lanes 0 .. count - 1 pass
+        lo += sum(passed) * step
+        n = step
+    return lo * chunk + (j - pref[lo])
+
+
+@pytest.mark.parametrize("lpr", [16, 32, 64])
+def test_group_live_at_is_the_live_token_map(lpr):
+    rng = np.random.default_rng(lpr)
+    chunk = 64
+    shapes = [1, 2, 3, 15, 16, 17, 63, 64, 65, 255, 256, 257, 512, 1000, 4096]
+    for chunks in shapes:
+        for kind in ("uniform", "sparse", "ones", "full"):
+            if kind == "uniform":
+                counts = rng.integers(0, chunk + 1, chunks)
+            elif kind == "sparse":  # mostly empty chunks: long runs of equal prefix values
+                counts = np.where(rng.random(chunks) < 0.05, rng.integers(1, chunk + 1, chunks), 0)
+            elif kind == "ones":
+                counts = np.ones(chunks, dtype=np.int64)
+            else:
+                counts = np.full(chunks, chunk)
+            lm = LiveMap(counts, chunk)
+            live = int(lm.pref[-1])
+            js = range(live) if live <= 3000 else sorted(set(rng.integers(0, live, 3000).tolist()) | {0, live - 1})
+            for j in js:
+                assert group_live_at(lm.pref, chunks, chunk, j, lpr) == lm.live_at(j), (chunks, kind, j)
+
+
+def test_the_scan_and_search_restatements_are_the_kernels():
+    for line in ("x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1",
+                 "x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2",
+                 "x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4",
+                 "x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8",
+                 "return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r1 : r2);",
+                 "const int32_t step = (n + LPR - 1) / LPR;",
+                 "const int32_t probe = lo + (lane + 1) * step;",
+                 "const bool pass = probe < m.chunks && m.pref[probe] <= j;",
+                 "lo += int32_t(__popcll(b)) * step;",
+                 "return int64_t(lo) * m.chunk + (j - m.pref[lo]);"):
+        assert line in SRC, line
+    assert SRC.count("wave_inclusive_sum(run)") == 2  # both kernels' scans
+    assert "__shfl_up" not in SRC
