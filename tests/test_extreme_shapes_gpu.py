@@ -40,6 +40,11 @@ GATHER = [
     ("one chunk of every token", torch.bfloat16, 3000, 128, 200, 200, 32, 32),
     ("chunks of one token", torch.bfloat16, 3000, 128, 150, 1, 16, 8),
     ("hd 1, widths 256", torch.float32, 1000, 1, 40, 8, 256, 256),
+    # the most chunks a workgroup's LDS scan takes (4096), in each lane-group size of
+    # the pair layout (16, 32 and 64 lanes: the deepest searches of the prefix)
+    ("4096 chunks of one token", torch.bfloat16, 3000, 128, 4096, 1, 8, 4),
+    ("4096 chunks of one token, 512-byte rows", torch.bfloat16, 3000, 256, 4096, 1, 4, 2),
+    ("4096 chunks of one token, 1 KiB rows", torch.bfloat16, 3000, 512, 4096, 1, 4, 4),
     # past the 4096 chunks a workgroup's LDS scan takes: the token-order layout
     ("5000 chunks of one token", torch.bfloat16, 3000, 128, 5000, 1, 8, 4),
 ]
@@ -57,3 +62,23 @@ def test_gather_extremes(case):
     run_case(wl, 62, per_chunk=True, stash=False)
     run_case(wl, 62, per_chunk=False, valid=max(1, chunk - 1), stash=False)
     run_compact(wl, 62)
+
+
+SPARSE = [
+    # name, hd: chunks of 4 tokens with 0 or 1 live (runs of empty chunks, so runs of
+    # equal prefix values), no stash: the pair layout's search at 16, 32 and 64 lanes
+    ("hd 128", 128),
+    ("hd 256", 256),
+    ("hd 512", 512),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE, ids=[c[0] for c in SPARSE])
+def test_gather_mostly_empty_chunks(case):
+    name, hd = case
+    wl = gen.GatherWorkload(name=f"mostly empty chunks, {name}", bank_dtype=torch.bfloat16, num_slots=2000,
+                            head_dim=hd, tokens=16000, chunk=4, valid_low=0, valid_high=1, width0=6, width1=3,
+                            idx_dtype=torch.int32, w_dtype=torch.bfloat16, bank_std=0.5)
+    print(wl.name, flush=True)
+    run_case(wl, 63, per_chunk=True, stash=False)
+    run_case(wl, 63, per_chunk=True)
