@@ -104,10 +104,10 @@ __device__ __forceinline__ void gather_batch(const E* __restrict__ bank, int64_t
     }
 }
 
-// Inclusive sum over a wavefront's 64 lanes: DPP shifts right by 1, 2, 4 and 8
-// lanes within each row of 16 lanes (a lane whose source lies outside its row adds
-// 0), then each row adds the totals of the rows before it, read from lanes 15, 31
-// and 47 into scalar registers.
+// Inclusive sum over a wavefront's 64 lanes, called with every lane active: DPP
+// shifts right by 1, 2, 4 and 8 lanes within each row of 16 lanes (a lane whose
+// source lies outside its row adds 0), then each row adds the totals of the rows
+// before it, read from lanes 15, 31 and 47 into scalar registers.
 __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
     x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
@@ -136,16 +136,6 @@ struct LiveMap {
     __device__ __forceinline__ int64_t live_token(int64_t j) const {
         const int64_t c = j / v;
         return c * chunk + (j - c * v);
-    }
-    // token of live index j < before(chunks): in the last chunk c with before(c) <= j
-    __device__ __forceinline__ int64_t live_at(int64_t j) const {
-        if (pref == nullptr) return live_token(j);
-        int64_t lo = 0, hi = chunks - 1;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) / 2;
-            if (before(mid) <= j) lo = mid; else hi = mid - 1;
-        }
-        return lo * chunk + (j - before(lo));
     }
     // token of padding index j < chunks chunk - before(chunks): in the last chunk c
     // with c chunk - before(c) <= j (the padding tokens before chunk c)
@@ -458,13 +448,14 @@ __device__ __forceinline__ int64_t operand_pair(int64_t i, int64_t run, int& op)
     return op ? i - run : i;
 }
 
-// LiveMap::live_at for the LPR lanes of one group, which share j: each step splits
-// the remaining chunks into LPR parts of step chunks, lane l tests whether part
-// l + 1 starts at or below j, and since the prefix never decreases the lanes that
-// pass are lanes 0 .. n - 1, so their count n (a ballot) names the part that
-// holds j. A probe past the remaining range fails (j lies before it), so each step
-// keeps a whole part: 512 chunks take 3 dependent LDS reads (16 lanes) or 2 (32
-// and 64) before the last, against 9 for a binary search.
+// Token of live index j < before(chunks): position j - before(c) of the last
+// chunk c with before(c) <= j, found by the LPR lanes of one group, which share j.
+// Each step splits the remaining chunks into LPR parts of step chunks, lane l
+// tests whether part l + 1 starts at or below j, and since the prefix never
+// decreases the lanes that pass are lanes 0 .. n - 1, so their count n (a ballot)
+// names the part that holds j. A probe past the remaining range fails (j lies
+// before it), so each step keeps a whole part: 512 chunks take 3 dependent LDS
+// reads (16 lanes) or 2 (32 and 64) before the last, against 9 for a binary search.
 template <int LPR>
 __device__ __forceinline__ int64_t group_live_at(const LiveMap& m, int64_t j, int lane) {
     if (m.pref == nullptr) return m.live_token(j);

@@ -123,7 +123,8 @@ def test_pair_batches_fit_a_group():
 
 
 class LiveMap:
-    """LiveMap: the live and padding tokens of a launch from its per-chunk counts."""
+    """LiveMap: the live and padding tokens of a launch from its per-chunk counts
+    (live_at, a bisection, is the reference that group_live_at is checked against)."""
 
     def __init__(self, counts, chunk):
         self.chunk = chunk
