@@ -440,9 +440,11 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 // end of a run). Operand-major, not interleaved by wavefront: the wavefronts in
 // flight then store rows of one output that follow one another, never the same
 // token's rows of both outputs at once. Two outputs allocated back to back lie a
-// power of two apart whenever the token count is one, and such paired stores
-// measured 9 % slower at 32768 tokens of 512-byte output rows (1 % slower shifted
-// by a few KiB, and no slower shifted by 1 MiB): they collide in the memory.
+// power of two apart when the token count is a power of two, and there such
+// paired stores collide in the memory: 32768 tokens of 512-byte output rows (the
+// outputs 16 MiB apart) took 204 us interleaved and 186 us operand-major, and
+// with the interleaved order a shift of one output by 512 B to 64 KiB did not
+// help where a shift by 1 MiB did.
 __device__ __forceinline__ int64_t operand_pair(int64_t i, int64_t run, int& op) {
     op = i >= run ? 1 : 0;
     return op ? i - run : i;
@@ -568,7 +570,8 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_pair_kernel(const GatherP
     }
     const int64_t live = m.before(m.chunks), pads = p.tokens - live;
     const int gpw = 64 / p.lpr;
-    // live pair indices: whole pairs of runs for two operands
+    // live pair indices: with two operands, one run per operand, each rounded up to
+    // whole wavefronts
     const int64_t live_ks = live * slices;
     const int64_t live_run = (live_ks + gpw - 1) / gpw * gpw;  // one operand's live pairs, whole wavefronts
     const int64_t live_pairs = NOPS == 2 ? 2 * live_run : live_ks;
