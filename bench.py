@@ -170,6 +170,10 @@ def parse_args(argv=None):
                    help="gather: bank rows of this many elements instead of the workload's (same slots and tokens)")
     p.add_argument("--bank-dtype", choices=["bf16", "f32"], default=None,
                    help="gather: bank element type instead of the workload's")
+    p.add_argument("--outputs-apart", type=int, default=None, metavar="ROWS",
+                   help="gather with two operands: both outputs in one allocation, operand 1's starting ROWS "
+                        "output rows after operand 0's last (0: back to back, the two a power of two apart "
+                        "when the token count is one); measures how the kernel depends on where the outputs lie")
     p.add_argument("--valid", default="per-chunk",
                    help="gather: per-chunk (the workload's per-chunk counts), all (every token live, no counts) "
                         "or N (one count N for every chunk, passed as the scalar valid)")
@@ -543,8 +547,14 @@ def bench_gather(torch, args, cfg_name, wl):
     two = args.gather in ("two-ops", "no-stash", "compact")
     with_stash = args.gather in ("two-ops", "one-op")
     compact = args.gather == "compact"
-    out0 = torch.empty((T, wl.head_dim), device=dev)
-    out1 = torch.empty((T, wl.head_dim), device=dev) if two else None
+    if args.outputs_apart is not None:
+        if not two or args.outputs_apart < 0:
+            raise SystemExit("bench.py: --outputs-apart takes a row count >= 0 and a two-operand gather")
+        both = torch.empty((2 * T + args.outputs_apart, wl.head_dim), device=dev)
+        out0, out1 = both[:T], both[T + args.outputs_apart:]
+    else:
+        out0 = torch.empty((T, wl.head_dim), device=dev)
+        out1 = torch.empty((T, wl.head_dim), device=dev) if two else None
     stash = torch.empty((T, wl.width0, wl.head_dim), dtype=wl.bank_dtype, device=dev) if with_stash else None
     if compact:
         kpos = gen.compact_positions(inp["idx0"], wl.chunk,
@@ -580,11 +590,15 @@ def bench_gather(torch, args, cfg_name, wl):
         name += f" [{T} tokens, valid {args.valid}]"
     if args.head_dim is not None or args.bank_dtype is not None:
         name += f" [head_dim {wl.head_dim}, {str(wl.bank_dtype).replace('torch.', '')} bank]"
+    if args.outputs_apart is not None:
+        name += f" [outputs {args.outputs_apart} rows apart]"
     config = {"workload": name, "tokens": T, "live_tokens": live, "valid": args.valid, "chunk": wl.chunk,
               "head_dim": wl.head_dim, "widths": [wl.width0, wl.width1 if two else 0],
               "stash": "compact" if compact else with_stash, "stash_rows": stash_rows,
               "slots": wl.num_slots, "bank_dtype": str(wl.bank_dtype).replace("torch.", ""),
               "launch": args.launch, "seed": args.seed}
+    if args.outputs_apart is not None:
+        config["outputs_apart_rows"] = args.outputs_apart
     value = T * K / (ms * 1e-3)
     return dict(value=value, unit="tokens/s", ms_step=ms_step, K=K, config=config, gbps=gbps,
                 row_bytes=row_bytes, cpu=cpu, tokens_per_s=value, tokens_per_launch=T, live_tokens=live)
@@ -875,7 +889,8 @@ def algorithmic_bytes(cfg_name: str, entry: str, seed: int = 0, gather: str = "t
 def ingest_profile(args) -> int:
     trace, fetch, write, copy_fetch, copy_write = args.ingest_profile
     if args.config == "c3" and (args.gather not in GATHER_SHAPES or args.valid != "per-chunk" or args.tokens
-                                or args.head_dim is not None or args.bank_dtype is not None):
+                                or args.head_dim is not None or args.bank_dtype is not None
+                                or args.outputs_apart is not None):
         raise SystemExit("bench.py: gather profiles are summarised for c3's own tokens and per-chunk counts, "
                          f"in the launch shapes {sorted(GATHER_SHAPES)}")
     kind = launch_kind(args.config, args.entry, args.gather)
@@ -1098,6 +1113,8 @@ def main(argv=None):
     args = parse_args(argv)
     if (args.head_dim is not None or args.bank_dtype is not None) and args.config != "c3":
         raise SystemExit("bench.py: --head-dim and --bank-dtype change the gather's bank (--config c3)")
+    if args.outputs_apart is not None and args.config != "c3":
+        raise SystemExit("bench.py: --outputs-apart places the gather's outputs (--config c3)")
     if args.ingest_profile:
         sys.path.insert(0, ROOT)
         return ingest_profile(args)
@@ -1151,8 +1168,9 @@ def main_one(torch, gen, args, wl) -> int:
         r = bench_gather(torch, args, args.config, wl)
     kind = launch_kind(args.config, args.entry, args.gather)
     traffic, kernel = stored_traffic(args.config, kind, r["tokens_per_launch"], r["live_tokens"])
-    if getattr(args, "head_dim", None) is not None or getattr(args, "bank_dtype", None) is not None:
-        traffic, kernel = None, None  # the stored figures are for the workload's own rows
+    if (getattr(args, "head_dim", None) is not None or getattr(args, "bank_dtype", None) is not None
+            or getattr(args, "outputs_apart", None) is not None):
+        traffic, kernel = None, None  # the stored figures are for the workload's own launch
     copy_gbps = streaming_copy_gbps(torch)
     out = {
         "metric": METRIC,

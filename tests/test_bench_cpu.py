@@ -375,3 +375,14 @@ def test_gather_bank_overrides_are_for_the_gather_and_never_profiled(tmp_path, m
     for flags in (["--head-dim", "256"], ["--bank-dtype", "f32"]):
         with pytest.raises(SystemExit, match="c3's own tokens"):
             bench.main(["--config", "c3", *flags, "--ingest-profile", t, f, w, cf, cw])
+
+
+def test_output_placement_is_for_the_gather_and_never_profiled(tmp_path, monkeypatch):
+    with pytest.raises(SystemExit, match="--config c3"):
+        bench.main(["--config", "c2", "--outputs-apart", "0"])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    t, f, w, cf, cw = (str(tmp_path / n) for n in ("trace", "fetch", "write", "cfetch", "cwrite"))
+    with pytest.raises(SystemExit, match="c3's own tokens"):
+        bench.main(["--config", "c3", "--outputs-apart", "0", "--ingest-profile", t, f, w, cf, cw])
+    assert bench.parse_args(["--config", "c3", "--outputs-apart", "2048"]).outputs_apart == 2048
+    assert bench.parse_args([]).outputs_apart is None
