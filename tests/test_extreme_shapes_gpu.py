@@ -20,6 +20,9 @@ DECODE = [
     ("bf16 hd 2 W = R = 256", torch.bfloat16, 3, 256, 2, 256, 256, 1, 2),
     ("bf16 hd 4095 odd long", torch.bfloat16, 3, 20, 4095, 3, 3, 3, 2),
     ("f32 many streams, one slot each", torch.float32, 3000, 1, 16, 1, 1, 1, 3),
+    # the multi-token compact loop's largest LDS: 32 row groups of 256-column slices,
+    # two partial buffers (about 83 KiB per workgroup)
+    ("bf16 hd 256 W = R = 256 (largest loop LDS)", torch.bfloat16, 4, 600, 256, 256, 256, 1, 3),
 ]
 
 
