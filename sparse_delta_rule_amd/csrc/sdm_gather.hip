@@ -167,14 +167,19 @@ __global__ __launch_bounds__(kThreads) void sdm_gather_kernel(const GatherParams
     const int op = pair - g * NOPS;          // operand
     // Workgroups are handed to the XCDs in turn (workgroup i to XCD i mod 8). In the
     // token order, give XCD x a contiguous share of the (token block, slice) pairs,
-    // so chunk positions (live heads, padding tails) mix evenly over the XCDs; in
-    // the live-token layout, where live blocks come first, keep the hardware's
-    // order, which deals them out to the XCDs in turn.
+    // so chunk positions (live heads, padding tails) mix evenly over the XCDs, and
+    // let each XCD start its walk through its share at a different point (x times
+    // an eighth of the share, plus x): the eight XCDs' concurrent stash stores then
+    // do not lie a power of two apart, as equal progress through shares of a
+    // power-of-two stash would put them (one operand with a stash +1.5 %). In the
+    // live-token layout, where live blocks come first, keep the hardware's order,
+    // which deals them out to the XCDs in turn.
     int64_t tblock = blockIdx.x, slice = blockIdx.y;
     if constexpr (!LIVE) {
         const int64_t n = int64_t(gridDim.x) * gridDim.y, i = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
         const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;
-        const int64_t j = x * q + (x < r ? x : r) + k;
+        const int64_t sz = q + (x < r ? 1 : 0);  // this XCD's share (>= 1 for every workgroup)
+        const int64_t j = x * q + (x < r ? x : r) + (k + x * (sz / 8 + 1)) % sz;
         tblock = j % gridDim.x;
         slice = j / gridDim.x;
     }

@@ -26,15 +26,29 @@ def cdiv(a, b):
 
 
 def xcd_share(i, n):
-    """sdm_gather_kernel's token order: workgroup i (run on XCD i mod 8) takes the
-    i // 8-th of a contiguous eighth of the n (token block, slice) pairs."""
+    """sdm_gather_kernel's token order: workgroup i (run on XCD i mod 8) takes a pair
+    of a contiguous eighth of the n (token block, slice) pairs, each XCD walking its
+    eighth from its own starting point."""
     q, r, x, k = n // 8, n % 8, i % 8, i // 8
-    return x * q + min(x, r) + k
+    sz = q + (1 if x < r else 0)
+    return x * q + min(x, r) + (k + x * (sz // 8 + 1)) % sz
 
 
 @pytest.mark.parametrize("n", list(range(1, 70)) + [255, 256, 257, 4096, 4097, 8191])
 def test_xcd_share_is_a_bijection(n):
     assert sorted(xcd_share(i, n) for i in range(n)) == list(range(n))
+
+
+def test_xcd_walks_at_equal_progress_are_not_a_power_of_two_apart():
+    # c3: 4096 token blocks of 8 tokens; the eight XCDs' blocks at the same step of
+    # their walks (the stash rows they store at about the same time)
+    n = 4096
+    for k in range(0, n // 8, 37):
+        pos = [xcd_share(x + 8 * k, n) for x in range(8)]
+        for a in range(8):
+            for b in range(a + 1, 8):
+                gap = abs(pos[a] - pos[b])
+                assert gap & (gap - 1) != 0, (k, a, b, gap)
 
 
 def test_xcd_share_gives_each_xcd_a_contiguous_run():
@@ -97,7 +111,8 @@ def test_the_restated_formulas_are_the_kernels():
                  "const int64_t live_pairs = NOPS == 2 ? 2 * live_run : live_ks;",
                  "pad_runs = (pad_pairs + kPadPairs - 1) / kPadPairs;",
                  "const int64_t q = n / 8, r = n % 8, x = i % 8, k = i / 8;",
-                 "const int64_t j = x * q + (x < r ? x : r) + k;",
+                 "const int64_t sz = q + (x < r ? 1 : 0);",
+                 "const int64_t j = x * q + (x < r ? x : r) + (k + x * (sz / 8 + 1)) % sz;",
                  "op = i >= run ? 1 : 0;",
                  "return op ? i - run : i;"):
         assert line in SRC, line
